@@ -1,0 +1,142 @@
+/*
+ * dsa.h - C ABI of the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+ *
+ * The path has three stages, as the DeepSeek-V3.2-Exp pages describe DSA:
+ *   1. the lightning indexer scores every earlier key for each query token
+ *      ("DeepSeek-V3.2-Exp" overview, section "架构 & 背后实现"; lightning-indexer
+ *      walk-through, step 3 "相关性得分计算"),
+ *   2. a per-query top-k keeps the k best-scoring positions
+ *      (walk-through step 4; "DeepSeek-V3.2-Exp解析" section 一.1),
+ *   3. MQA-mode attention over the MLA latent cache runs on the selected rows only
+ *      ("DeepSeek-V3.2 explained", sections 二.1 and 二.4: DSA(q_t,K,V) = attention of q_t over
+ *      the rows picked by TopK(Indexer(q_t,K)); one 576-wide latent row per token shared by
+ *      every head).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Ownership: the caller allocates every buffer (inputs, outputs, workspace) in device
+ *    memory.  The library never allocates, frees or synchronises; all work is enqueued on
+ *    the caller's stream.  The library keeps no mutable global state and is thread-safe.
+ *  - Batches: a batch holds n_seqs sequences.  Sequence b owns query rows
+ *    [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1]) of the packed arrays.  Its
+ *    queries are the last len_q(b) tokens of its key sequence, so query row i of b sits at
+ *    position p = len_k(b) - len_q(b) + (i - cu_q[b]) and sees keys at positions 0..p
+ *    (causal, the query's own position included).  Prefill is one sequence with
+ *    len_q = len_k; decode is len_q = 1 per sequence.
+ *  - Validation: every argument is checked on the host before anything is enqueued (null
+ *    pointers, unsupported dims, topk outside [1, 2048], len_q > len_k, non-monotone or
+ *    non-zero-based offsets, pointers not 16-byte aligned, strides too small or not a
+ *    multiple of 4, workspace too small).  On error nothing is enqueued and nothing is
+ *    written.  A failed kernel launch returns DSA_ERR_HIP.
+ *  - Supported dims: (n_idx_heads, idx_dim, n_heads, qk_dim, v_dim) is either the
+ *    DeepSeek-V3.2-Exp shape (64, 128, 128, 576, 512) or the tiny test shape
+ *    (4, 32, 8, 80, 64); topk may be any value in [1, 2048]; sm_scale any positive
+ *    finite number.  Anything else returns DSA_ERR_UNSUPPORTED.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,
+    DSA_ERR_UNSUPPORTED = 2,
+    DSA_ERR_WORKSPACE = 3,
+    DSA_ERR_HIP = 4
+} dsa_status;
+
+/* Shape of one DSA layer. */
+typedef struct {
+    int32_t n_idx_heads; /* H_I: indexer heads (64)                                  */
+    int32_t idx_dim;     /* d_I: indexer head dim (128)                              */
+    int32_t topk;        /* k: selected positions per query (2048)                   */
+    int32_t n_heads;     /* H: attention heads sharing each latent row (128)         */
+    int32_t qk_dim;      /* latent row width used for the logits (576 = 512 + 64)    */
+    int32_t v_dim;       /* value width = leading part of the latent row (512)       */
+    float sm_scale;      /* softmax scale applied to q.c (1/sqrt(192))               */
+} dsa_dims;
+
+/* Sequence layout of a batch.  The host and device arrays must hold the same values. */
+typedef struct {
+    int32_t n_seqs;           /* B >= 1                                               */
+    const int32_t* cu_q_host; /* [B+1] query row offsets, host memory, cu_q[0] = 0    */
+    const int32_t* cu_k_host; /* [B+1] key row offsets, host memory, cu_k[0] = 0      */
+    const int32_t* cu_q_dev;  /* [B+1] the same offsets in device memory              */
+    const int32_t* cu_k_dev;  /* [B+1]                                                */
+} dsa_batch;
+
+/* Bytes of workspace that dsa_forward (and dsa_sparse_mqa, which needs less) uses by
+ * default for this batch.  dsa_forward also accepts a smaller workspace down to
+ * dsa_workspace_min; it then processes fewer query rows per pass. */
+dsa_status dsa_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
+dsa_status dsa_workspace_min(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
+
+/* Lightning indexer (stage 1).
+ * For every query row i and every key position s in [0, p_i]:
+ *   I[i,s] = k_scale[s] * sum_j (w[i,j] * q_scale[i,j]) * ReLU( q8[i,j,:] . k8[s,:] )
+ * where the dot product runs over FP8 e4m3fn codes (exact products, fp32 accumulation)
+ * and j over the n_idx_heads heads.  Both scales are positive, so they factor out of the
+ * ReLU unchanged ("DeepSeek-V3.2-Exp" overview, indexer score; walk-through step 2 for the
+ * cached FP8 keys and their scale, step 3 for ReLU and the weighted head sum).
+ *   q8      [T, n_idx_heads, idx_dim] uint8 e4m3fn codes (T = cu_q[B])
+ *   q_scale [T, n_idx_heads] float32 (> 0),  w [T, n_idx_heads] float32
+ *   k8      [S, idx_dim] uint8 e4m3fn codes (S = cu_k[B]),  k_scale [S] float32 (> 0)
+ *   scores  float32; row i starts at scores + i*score_stride and receives entries
+ *           0..p_i; entries past p_i are left untouched.  score_stride >= max p_i + 1,
+ *           multiple of 4. */
+dsa_status dsa_indexer_scores(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                              const float* q_scale, const float* w, const uint8_t* k8,
+                              const float* k_scale, float* scores, int64_t score_stride,
+                              hipStream_t stream);
+
+/* Top-k selection (stage 2).
+ * For query row i with n = p_i + 1 valid scores at scores + i*score_stride, select the
+ * min(k, n) positions with the largest scores ("DeepSeek-V3.2-Exp" deep dive, section 2.2
+ * on fine-grained token selection: only the k best-scoring positions are kept).
+ * Ranking: larger first, -0 equals +0, NaN below -inf, equal scores -> lower position first.
+ * idx [T, topk] int32 receives the selected positions in ascending order followed by -1
+ * in the unused slots.  The result is unique, so it is bit-exact and deterministic. */
+dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* scores,
+                    int64_t score_stride, int32_t* idx, hipStream_t stream);
+
+/* Sparse MQA over the latent cache (stage 3).
+ * For query row i and head h, over the slots of idx[i,:] that are not -1 (positions in
+ * the row's own sequence; trusted to lie in [0, len_k)):
+ *   z_s = sm_scale * q[i,h,:qk_dim] . kv[s,:qk_dim]
+ *   out[i,h,:] = sum_s softmax(z)_s * kv[s,:v_dim],   lse[i,h] = ln sum_s exp(z_s)
+ * Every head reads the same latent rows (MQA mode).  A row without valid slots gets
+ * out = 0 and lse = -inf.
+ *   q   [T, n_heads, qk_dim] bf16 bits,  kv [S, qk_dim] bf16 bits,  idx [T, topk] int32
+ *   out [T, n_heads, v_dim] bf16 bits,   lse [T, n_heads] float32 or NULL
+ *   ws / ws_bytes: workspace (may be NULL/0 unless dsa_workspace_size asks for it; it is
+ *   used to split rows over several workgroups when T is small, e.g. decode). */
+dsa_status dsa_sparse_mqa(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
+                          const uint16_t* kv, const int32_t* idx, uint16_t* out, float* lse,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole hot path: indexer -> top-k -> sparse MQA, on the caller's stream.
+ * Inputs as above.  Scores live only in the workspace, one pass of query rows at a time;
+ * the full L x L score matrix never exists.  Rows with p + 1 <= topk skip the indexer and
+ * the selection (their index set is every earlier position; the result is the same).
+ *   idx_out [T, topk] int32 or NULL (then the selected positions stay in the workspace). */
+dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                       const float* q_scale, const float* w, const uint8_t* k8,
+                       const float* k_scale, const uint16_t* q, const uint16_t* kv,
+                       uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Static description of a status code. */
+const char* dsa_status_string(dsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,189 @@
+"""Thin Python binding of ``libdsa.so``, the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+
+Argument marshalling only: torch tensors are passed to the C ABI (``include/dsa.h``) as raw
+device pointers together with the current HIP stream; every step of the computation runs in
+the library's HIP kernels.  There is no fallback: if the library is missing, importing the
+functions raises.
+
+Entry points mirror the C ABI: ``indexer_scores``, ``topk``, ``sparse_mqa``, ``forward``,
+``workspace_size`` / ``workspace_min``.  A batch is described by its query and key row offsets
+(``cu_q``, ``cu_k``: B + 1 integers); see ``include/dsa.h`` for the layouts.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = ["DsaError", "Dims", "Batch", "lib", "library_path", "indexer_scores", "topk",
+           "sparse_mqa", "forward", "workspace_size", "workspace_min", "PROD_DIMS", "TINY_DIMS",
+           "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdsa.so")
+_lib = None
+
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
+          4: "DSA_ERR_HIP"}
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("qk_dim", ctypes.c_int32),
+                ("v_dim", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+    @classmethod
+    def of(cls, d) -> "Dims":
+        """From any object with the same attribute names (e.g. dsa_inputs.Dims)."""
+        return cls(d.n_idx_heads, d.idx_dim, d.topk, d.n_heads, d.qk_dim, d.v_dim, d.sm_scale)
+
+
+class _CBatch(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("cu_q_host", ctypes.c_void_p),
+                ("cu_k_host", ctypes.c_void_p), ("cu_q_dev", ctypes.c_void_p),
+                ("cu_k_dev", ctypes.c_void_p)]
+
+
+class Batch:
+    """Sequence offsets in host and device memory, kept alive together."""
+
+    def __init__(self, cu_q, cu_k, device="cuda"):
+        self.cu_q = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int32))
+        self.cu_k = np.ascontiguousarray(np.asarray(cu_k, dtype=np.int32))
+        if self.cu_q.shape != self.cu_k.shape or self.cu_q.ndim != 1 or len(self.cu_q) < 2:
+            raise ValueError("cu_q and cu_k must be 1-D with the same length >= 2")
+        self.cu_q_dev = torch.from_numpy(self.cu_q).to(device)
+        self.cu_k_dev = torch.from_numpy(self.cu_k).to(device)
+        self.c = _CBatch(len(self.cu_q) - 1, self.cu_q.ctypes.data, self.cu_k.ctypes.data,
+                         self.cu_q_dev.data_ptr(), self.cu_k_dev.data_ptr())
+
+    @property
+    def n_seqs(self) -> int:
+        return len(self.cu_q) - 1
+
+    @property
+    def n_q(self) -> int:
+        return int(self.cu_q[-1])
+
+    @property
+    def n_k(self) -> int:
+        return int(self.cu_k[-1])
+
+    @property
+    def max_len_k(self) -> int:
+        return int(np.diff(self.cu_k).max())
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded ``libdsa.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m sparse_attention_long_lightning_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, S, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
+        st = ctypes.c_int
+        for name, args in {
+            "dsa_workspace_size": [P, P, P],
+            "dsa_workspace_min": [P, P, P],
+            "dsa_indexer_scores": [P, P, P, P, P, P, P, P, I64, P],
+            "dsa_topk": [P, P, P, I64, P, P],
+            "dsa_sparse_mqa": [P, P, P, P, P, P, P, P, S, P],
+            "dsa_forward": [P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
+        }.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = st
+        L.dsa_status_string.argtypes = [st]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise DsaError(status, where)
+
+
+def _dims(dims) -> Dims:
+    return dims if isinstance(dims, Dims) else Dims.of(dims)
+
+
+def workspace_size(dims, batch: Batch) -> int:
+    out = ctypes.c_size_t(0)
+    d = _dims(dims)
+    _check(lib().dsa_workspace_size(ctypes.byref(d), ctypes.byref(batch.c), ctypes.byref(out)),
+           "dsa_workspace_size")
+    return int(out.value)
+
+
+def workspace_min(dims, batch: Batch) -> int:
+    out = ctypes.c_size_t(0)
+    d = _dims(dims)
+    _check(lib().dsa_workspace_min(ctypes.byref(d), ctypes.byref(batch.c), ctypes.byref(out)),
+           "dsa_workspace_min")
+    return int(out.value)
+
+
+def indexer_scores(dims, batch: Batch, q8, q_scale, w, k8, k_scale, scores, score_stride: int,
+                   stream=None):
+    d = _dims(dims)
+    _check(lib().dsa_indexer_scores(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q8), _ptr(q_scale),
+                                    _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(scores),
+                                    int(score_stride), _stream(stream)), "dsa_indexer_scores")
+    return scores
+
+
+def topk(dims, batch: Batch, scores, score_stride: int, idx, stream=None):
+    d = _dims(dims)
+    _check(lib().dsa_topk(ctypes.byref(d), ctypes.byref(batch.c), _ptr(scores), int(score_stride),
+                          _ptr(idx), _stream(stream)), "dsa_topk")
+    return idx
+
+
+def sparse_mqa(dims, batch: Batch, q, kv, idx, out, lse=None, ws=None, stream=None):
+    d = _dims(dims)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dsa_sparse_mqa(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q), _ptr(kv),
+                                _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                _stream(stream)), "dsa_sparse_mqa")
+    return out
+
+
+def forward(dims, batch: Batch, q8, q_scale, w, k8, k_scale, q, kv, out, lse=None, idx_out=None,
+            ws=None, stream=None):
+    d = _dims(dims)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dsa_forward(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q8), _ptr(q_scale),
+                             _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), _ptr(out),
+                             _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)),
+           "dsa_forward")
+    return out
+
+
+PROD_DIMS = Dims(64, 128, 2048, 128, 576, 512, 1.0 / np.sqrt(192.0))
+TINY_DIMS = Dims(4, 32, 32, 8, 80, 64, 1.0 / np.sqrt(80.0))

@@ -1,0 +1,321 @@
+// C ABI of the DSA hot path: argument validation, workspace policy and the launch sequence
+// of dsa_forward (lightning indexer -> top-k -> sparse MQA, "DeepSeek-V3.2-Exp解析" section
+// 一.1 three-stage workflow).  Nothing here allocates, frees or synchronises.
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstdio>
+
+#include "dsa.h"
+#include "internal.hpp"
+
+using namespace dsa;
+
+namespace {
+
+constexpr int kDefaultChunkRows = 8192;  // query rows per prefill pass at the default size
+constexpr int kRowGranule = 8;           // prefill passes cover multiples of this many rows
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Batch {
+    int B = 0;
+    int T = 0;  // total query rows
+    int S = 0;  // total key rows
+    int max_lk = 0;
+    int max_lq = 0;
+    bool decode = false;  // every sequence has exactly one query row
+    const dsa_batch* raw = nullptr;
+    int lq(int b) const { return raw->cu_q_host[b + 1] - raw->cu_q_host[b]; }
+    int lk(int b) const { return raw->cu_k_host[b + 1] - raw->cu_k_host[b]; }
+};
+
+bool debug_log() {
+    static const bool on = [] {
+        const char* e = getenv("DSA_LOG");
+        return e != nullptr && e[0] == '1';
+    }();
+    return on;
+}
+
+dsa_status check_dims(const dsa_dims* d, Shape* shape) {
+    if (d == nullptr) return DSA_ERR_INVALID_ARG;
+    if (d->topk < 1 || d->topk > kMaxTopk) return DSA_ERR_INVALID_ARG;
+    if (!(d->sm_scale > 0.f) || !std::isfinite(d->sm_scale)) return DSA_ERR_INVALID_ARG;
+    if (d->n_idx_heads == 64 && d->idx_dim == 128 && d->n_heads == 128 && d->qk_dim == 576 &&
+        d->v_dim == 512) {
+        *shape = Shape::Prod;
+        return DSA_OK;
+    }
+    if (d->n_idx_heads == 4 && d->idx_dim == 32 && d->n_heads == 8 && d->qk_dim == 80 &&
+        d->v_dim == 64) {
+        *shape = Shape::Tiny;
+        return DSA_OK;
+    }
+    return DSA_ERR_UNSUPPORTED;
+}
+
+dsa_status check_batch(const dsa_batch* b, Batch* out) {
+    if (b == nullptr || b->n_seqs < 1 || b->cu_q_host == nullptr || b->cu_k_host == nullptr ||
+        b->cu_q_dev == nullptr || b->cu_k_dev == nullptr)
+        return DSA_ERR_INVALID_ARG;
+    if (b->cu_q_host[0] != 0 || b->cu_k_host[0] != 0) return DSA_ERR_INVALID_ARG;
+    Batch r;
+    r.raw = b;
+    r.B = b->n_seqs;
+    r.decode = true;
+    for (int i = 0; i < b->n_seqs; ++i) {
+        const int64_t lq = (int64_t)b->cu_q_host[i + 1] - b->cu_q_host[i];
+        const int64_t lk = (int64_t)b->cu_k_host[i + 1] - b->cu_k_host[i];
+        if (lq < 0 || lk < 0 || lq > lk) return DSA_ERR_INVALID_ARG;
+        if (lq > r.max_lq) r.max_lq = (int)lq;
+        if (lk > r.max_lk) r.max_lk = (int)lk;
+        if (lq != 1) r.decode = false;
+    }
+    r.T = b->cu_q_host[b->n_seqs];
+    r.S = b->cu_k_host[b->n_seqs];
+    *out = r;
+    return DSA_OK;
+}
+
+// Split count of the sparse MQA for a batch of T rows: enough workgroups to cover the chip
+// when there are few rows (decode), at least 128 selected slots per split.
+int mqa_splits(int T, int topk) {
+    if (T <= 0 || T >= 128) return 1;
+    int n = (256 + T - 1) / T;
+    const int cap = (topk + 127) / 128;
+    if (n > cap) n = cap;
+    if (n > 8) n = 8;
+    return n < 1 ? 1 : n;
+}
+
+int64_t score_stride_for(const Batch& bt) { return ((int64_t)bt.max_lk + 3) & ~(int64_t)3; }
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+struct ForwardPlan {
+    int64_t stride = 0;
+    int chunk = 0;  // prefill rows per pass
+    size_t scores_off = 0, idx_off = 0, mqa_off = 0, total = 0;
+};
+
+// Workspace layout of dsa_forward: [scores | idx (when idx_out is NULL) | MQA partials].
+ForwardPlan plan_forward(const dsa_dims* d, Shape shape, const Batch& bt, int chunk) {
+    ForwardPlan p;
+    p.stride = score_stride_for(bt);
+    if (bt.decode) {
+        p.chunk = bt.T;
+        p.scores_off = 0;
+        p.idx_off = align_up((size_t)bt.T * p.stride * sizeof(float));
+        p.mqa_off = p.idx_off + align_up((size_t)bt.T * d->topk * sizeof(int32_t));
+        p.total = p.mqa_off + mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, d->topk));
+    } else {
+        p.chunk = chunk;
+        p.idx_off = align_up((size_t)chunk * p.stride * sizeof(float));
+        p.mqa_off = p.idx_off + align_up((size_t)chunk * d->topk * sizeof(int32_t));
+        p.total = p.mqa_off;
+    }
+    return p;
+}
+
+int default_chunk(const Batch& bt) {
+    int c = bt.max_lq < kDefaultChunkRows ? bt.max_lq : kDefaultChunkRows;
+    return c < 1 ? 1 : c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s) {
+    switch (s) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: unsupported dims";
+        case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace too small";
+        case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP launch failure";
+    }
+    return "unknown dsa_status";
+}
+
+dsa_status dsa_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if (bytes == nullptr) return DSA_ERR_INVALID_ARG;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    const ForwardPlan p = plan_forward(dims, shape, bt, default_chunk(bt));
+    size_t need = p.total;
+    const size_t mqa = mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, dims->topk));
+    if (mqa > need) need = mqa;
+    *bytes = need;
+    return DSA_OK;
+}
+
+dsa_status dsa_workspace_min(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if (bytes == nullptr) return DSA_ERR_INVALID_ARG;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    const int c = bt.max_lq < kRowGranule ? (bt.max_lq < 1 ? 1 : bt.max_lq) : kRowGranule;
+    const ForwardPlan p = plan_forward(dims, shape, bt, c);
+    size_t need = p.total;
+    const size_t mqa = mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, dims->topk));
+    if (mqa > need) need = mqa;
+    *bytes = need;
+    return DSA_OK;
+}
+
+dsa_status dsa_indexer_scores(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                              const float* q_scale, const float* w, const uint8_t* k8,
+                              const float* k_scale, float* scores, int64_t score_stride,
+                              hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!q8 || !q_scale || !w || !k8 || !k_scale || !scores) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q8) || !aligned16(q_scale) || !aligned16(w) || !aligned16(k8) ||
+        !aligned16(k_scale) || !aligned16(scores))
+        return DSA_ERR_INVALID_ARG;
+    if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
+    IndexerArgs a{shape, q8, q_scale, w, k8, k_scale, scores, score_stride};
+    if (bt.decode)
+        return hip_status(launch_indexer_decode(a, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, stream));
+    for (int b = 0; b < bt.B; ++b) {
+        const int lq = bt.lq(b), lk = bt.lk(b);
+        if (lq == 0) continue;
+        const int row0 = batch->cu_q_host[b];
+        hipError_t e = launch_indexer_prefill(a, row0, lq, lk - lq, batch->cu_k_host[b],
+                                              scores + (int64_t)row0 * score_stride, stream);
+        if (e != hipSuccess) return DSA_ERR_HIP;
+    }
+    return DSA_OK;
+}
+
+dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* scores,
+                    int64_t score_stride, int32_t* idx, hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!scores || !idx || !aligned16(scores) || !aligned16(idx)) return DSA_ERR_INVALID_ARG;
+    if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
+    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
+    return hip_status(launch_topk(scores, score_stride, idx, dims->topk, map, bt.T, stream));
+}
+
+dsa_status dsa_sparse_mqa(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
+                          const uint16_t* kv, const int32_t* idx, uint16_t* out, float* lse,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!q || !kv || !idx || !out) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(idx) || !aligned16(out) ||
+        (lse != nullptr && !aligned16(lse)))
+        return DSA_ERR_INVALID_ARG;
+    const int n_split = mqa_splits(bt.T, dims->topk);
+    const size_t need = mqa_split_bytes(shape, bt.T, n_split);
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return DSA_ERR_WORKSPACE;
+    MqaArgs a{shape, q, kv, idx, dims->topk, out, lse, dims->sm_scale};
+    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
+    return hip_status(launch_sparse_mqa(a, map, bt.T, n_split, ws, stream));
+}
+
+dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                       const float* q_scale, const float* w, const uint8_t* k8,
+                       const float* k_scale, const uint16_t* q, const uint16_t* kv,
+                       uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!q8 || !q_scale || !w || !k8 || !k_scale || !q || !kv || !out) return DSA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q8, q_scale, w, k8, k_scale, q, kv, out};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return DSA_ERR_INVALID_ARG;
+    if ((lse != nullptr && !aligned16(lse)) || (idx_out != nullptr && !aligned16(idx_out)))
+        return DSA_ERR_INVALID_ARG;
+    if (ws == nullptr || !aligned16(ws)) return DSA_ERR_WORKSPACE;
+    const int topk = dims->topk;
+    uint8_t* wsb = (uint8_t*)ws;
+
+    if (bt.decode) {
+        const ForwardPlan p = plan_forward(dims, shape, bt, bt.T);
+        if (ws_bytes < p.total) return DSA_ERR_WORKSPACE;
+        float* sc = (float*)(wsb + p.scores_off);
+        int32_t* ix = idx_out ? idx_out : (int32_t*)(wsb + p.idx_off);
+        IndexerArgs ia{shape, q8, q_scale, w, k8, k_scale, sc, p.stride};
+        RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
+        const int n_split = mqa_splits(bt.T, topk);
+        MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale};
+        if (debug_log())
+            fprintf(stderr, "[dsa] decode B=%d max_len_k=%d stride=%lld splits=%d\n", bt.B, bt.max_lk,
+                    (long long)p.stride, n_split);
+        hipError_t e = launch_indexer_decode(ia, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, stream);
+        if (e == hipSuccess) e = launch_topk(sc, p.stride, ix, topk, map, bt.T, stream);
+        if (e == hipSuccess) e = launch_sparse_mqa(ma, map, bt.T, n_split, wsb + p.mqa_off, stream);
+        return hip_status(e);
+    }
+
+    // Prefill: passes of `chunk` query rows per sequence.
+    const int64_t stride = score_stride_for(bt);
+    auto bytes_for = [&](int c) {
+        return align_up((size_t)c * stride * sizeof(float)) +
+               (idx_out ? 0 : align_up((size_t)c * topk * sizeof(int32_t)));
+    };
+    const size_t per_row = (size_t)stride * sizeof(float) + (idx_out ? 0 : (size_t)topk * 4);
+    int64_t c64 = (int64_t)(ws_bytes / per_row);
+    int chunk = (int)(c64 < bt.max_lq ? c64 : bt.max_lq);
+    if (chunk > kRowGranule) chunk -= chunk % kRowGranule;
+    while (chunk > 0 && bytes_for(chunk) > ws_bytes) chunk -= chunk > kRowGranule ? kRowGranule : 1;
+    const int min_chunk = bt.max_lq < kRowGranule ? bt.max_lq : kRowGranule;
+    if (chunk < 1 || chunk < min_chunk) return DSA_ERR_WORKSPACE;
+    const ForwardPlan p = plan_forward(dims, shape, bt, chunk);
+    float* sc = (float*)(wsb + p.scores_off);
+    int32_t* ix_ws = (int32_t*)(wsb + p.idx_off);
+    IndexerArgs ia{shape, q8, q_scale, w, k8, k_scale, sc, p.stride};
+    if (debug_log())
+        fprintf(stderr, "[dsa] prefill B=%d T=%d chunk=%d stride=%lld\n", bt.B, bt.T, chunk,
+                (long long)p.stride);
+    for (int b = 0; b < bt.B; ++b) {
+        const int lq = bt.lq(b), lk = bt.lk(b);
+        const int qb = batch->cu_q_host[b], kb = batch->cu_k_host[b];
+        const int pos0 = lk - lq;
+        for (int r0 = 0; r0 < lq; r0 += chunk) {
+            const int r1 = r0 + chunk < lq ? r0 + chunk : lq;
+            // rows with p + 1 <= topk keep every earlier position: no scores needed
+            int rsel = topk - pos0;
+            if (rsel < r0) rsel = r0;
+            hipError_t e = hipSuccess;
+            if (rsel < r1)
+                e = launch_indexer_prefill(ia, qb + rsel, r1 - rsel, pos0 + rsel, kb,
+                                           sc + (int64_t)(rsel - r0) * p.stride, stream);
+            int32_t* ix = idx_out ? idx_out + (int64_t)(qb + r0) * topk : ix_ws;
+            RowMap map{nullptr, nullptr, 1, qb + r0, pos0 + r0, kb};
+            if (e == hipSuccess) e = launch_topk(sc, p.stride, ix, topk, map, r1 - r0, stream);
+            MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale};
+            if (e == hipSuccess) e = launch_sparse_mqa(ma, map, r1 - r0, 1, nullptr, stream);
+            if (e != hipSuccess) return DSA_ERR_HIP;
+        }
+    }
+    return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Host-side declarations shared between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dsa {
+
+enum class Shape { Prod, Tiny };
+
+struct IndexerArgs {
+    Shape shape;
+    const uint8_t* q8;
+    const float* q_scale;
+    const float* w;
+    const uint8_t* k8;
+    const float* k_scale;
+    float* scores;
+    int64_t score_stride;
+};
+
+// Prefill tiles for rows [row0, row0 + n_rows) of one sequence whose first row sits at
+// position pos0 and whose key rows start at kbase.  Row i of the launch writes
+// scores + i * score_stride.
+hipError_t launch_indexer_prefill(const IndexerArgs& a, int row0, int n_rows, int pos0,
+                                  int kbase, float* scores, hipStream_t st);
+// Decode: one query row per sequence (cu_q[b+1] - cu_q[b] == 1); row cu_q[b] of the scores.
+hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,
+                                 const int32_t* cu_q, const int32_t* cu_k, hipStream_t st);
+
+// Top-k over n_rows score rows; row i reads scores + i * stride and writes idx + i * topk.
+hipError_t launch_topk(const float* scores, int64_t stride, int32_t* idx, int topk,
+                       const RowMap& map, int n_rows, hipStream_t st);
+
+struct MqaArgs {
+    Shape shape;
+    const uint16_t* q;
+    const uint16_t* kv;
+    const int32_t* idx;  // row i of the launch at idx + i * topk
+    int topk;
+    uint16_t* out;       // indexed by packed query row
+    float* lse;          // nullable, indexed by packed query row
+    float sm_scale;
+};
+
+// Bytes of split partials for n_rows rows split n_split ways.
+size_t mqa_split_bytes(Shape shape, int n_rows, int n_split);
+// Sparse MQA for n_rows rows; n_split > 1 splits each row's slots over workgroups and
+// merges the partials (ws must hold mqa_split_bytes).
+hipError_t launch_sparse_mqa(const MqaArgs& a, const RowMap& map, int n_rows, int n_split,
+                             void* ws, hipStream_t st);
+
+}  // namespace dsa

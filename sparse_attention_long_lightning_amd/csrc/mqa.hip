@@ -1,0 +1,426 @@
+// Sparse MQA over the MLA latent cache on gfx950 (core attention of DSA on the top-k rows;
+// DeepSeek-V3.2 explained, sections 二.1 and 二.4; DeepSeek-V3.2-Exp overview, module table).
+//
+// For query row t and head h, over the selected latent rows c_s (576 = 512 latent + 64
+// rope; every head shares the row):
+//     z_s = sm * <q[t,h,:], c_s>,  out[t,h,:] = sum_s softmax(z)_s c_s[:512],  lse = ln sum e^z
+//
+// One workgroup owns one query row and all its heads: wave w owns heads 32w..32w+31, so each
+// gathered latent row is staged in LDS once and reused by every head.  Per block of 32
+// selected rows:
+//   S^T = C Q^T   v_mfma_f32_32x32x16_bf16, A = latent rows from LDS (M = 32 rows),
+//                 B = the wave's 32 query heads kept in registers for the whole row (N = heads)
+//   online softmax in base 2 on S^T: lane l owns head l%32, so the running max / sum are
+//                 per-lane values (one exchange with lane l^32 per block)
+//   O^T += V^T P^T   A = value columns read from the same row-major LDS block with the
+//                 gfx950 transpose read (ds_read_b64_tr_b16), B = P^T straight from the S^T
+//                 accumulators (row order of S^T is chosen so that each lane already holds
+//                 8 consecutive rows per MFMA k-slice).
+// Rescaling of O is lazy: the running max only moves when a block's max exceeds it by more
+// than 8 (factor 256 of headroom in fp32), which keeps the arithmetic exact up to rounding.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kBlk = 32;  // selected rows per LDS block
+
+// LDS image of one block of kBlk latent rows, split in two regions of 16-byte chunks:
+// the value part (first DV columns) and the rope part (the remaining DQK - DV columns).
+// Rows are written by direct global->LDS loads, 64 chunks (1 KiB) per wave instruction:
+//  - a region with 64 chunks per row gets one row per instruction and a 16-byte pad per row,
+//  - a narrower region packs 64/NC rows per instruction and XOR-swizzles the chunk index
+//    of each row instead, so rows read together by one MFMA operand land in different banks.
+template <int NC>
+struct Region {
+    static constexpr bool ONE_ROW = NC == 64;
+    static constexpr int ROWS_PER_INSTR = 64 / NC;
+    static constexpr int PITCH = ONE_ROW ? NC * 16 + 16 : NC * 16;
+    static constexpr int BYTES = kBlk * PITCH;
+    static constexpr int INSTRS = kBlk / ROWS_PER_INSTR;
+    static_assert(NC == 64 || NC == 8 || NC == 2, "unsupported region width");
+    __device__ static __forceinline__ int swz(int r) {
+        return ONE_ROW ? 0 : (((r & 3) | ((r & 8) >> 1)) & (NC - 1));
+    }
+    // byte offset of logical chunk c of row r
+    __device__ static __forceinline__ int chunk(int r, int c) { return r * PITCH + 16 * (c ^ swz(r)); }
+};
+
+template <int H, int DQK, int DV>
+struct MqaCfg {
+    static constexpr int THREADS = 256;        // 4 waves: 2 head groups x 2 halves
+    static constexpr int NW = 4;
+    static constexpr int NHH = (H + 63) / 64;  // workgroups per query row, 64 heads each
+    static constexpr int KS = DQK / 16;        // k-slices of the logit product
+    static constexpr int KS0 = (KS + 1) / 2;   // slices of half 0 (half 1 takes the rest)
+    static constexpr int KSV = DV / 16;        // k-slices that fall in the value region
+    static constexpr int VT = DV / 32;         // 32-wide value tiles
+    static constexpr int VT0 = VT / 2;         // value tiles per half
+    using RV = Region<DV * 2 / 16>;
+    using RR = Region<(DQK - DV) * 2 / 16>;
+    static constexpr int BUF = RV::BYTES + RR::BYTES;
+    static constexpr int INSTRS = RV::INSTRS + RR::INSTRS;
+    static constexpr int ROW_BYTES = DQK * 2;  // bytes of one latent row in memory
+    static constexpr int VBYTES = DV * 2;      // bytes of its value part
+    static_assert(DQK % 16 == 0 && DV % 64 == 0, "unsupported latent widths");
+    static_assert(NHH <= 2, "at most 128 heads");
+};
+
+__device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ v4s ds_read_tr16(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+}
+
+// Workgroup barrier that orders LDS accesses only: in-flight direct global->LDS loads into
+// the other buffer are not waited for (the fence of a full __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS access moves above the barrier
+}
+
+__device__ __forceinline__ uint16_t f2bf(float x) {
+    __bf16 b = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// Issues the direct loads of one block into the LDS image at `buf`: lane l%32 holds the
+// latent row index of block row l%32 in `sidx` (-1 for an empty slot) and bit r of `vmask`
+// tells whether block row r is occupied.  Empty rows are zero-filled so that they contribute
+// exact zeros to both products.
+template <class C>
+__device__ __forceinline__ void gather_block(uint8_t* buf, const uint8_t* kvb, int sidx,
+                                             uint32_t vmask, int wv, int lane) {
+    using RV = typename C::RV;
+    using RR = typename C::RR;
+    for (int I = wv; I < C::INSTRS; I += C::NW) {  // same trip count on every lane
+        const bool rope = I >= RV::INSTRS;
+        const int Ir = rope ? I - RV::INSTRS : I;
+        const int rows = rope ? RR::ROWS_PER_INSTR : RV::ROWS_PER_INSTR;
+        const int ncol = 64 / rows;  // chunks per row in this region
+        const int r = Ir * rows + lane / ncol;
+        const int p = lane % ncol;
+        const int c = rope ? (p ^ RR::swz(r)) : (p ^ RV::swz(r));
+        const int s = __shfl(sidx, r);
+        uint8_t* dst = rope ? buf + RV::BYTES + Ir * (RR::ONE_ROW ? RR::PITCH : 1024)
+                            : buf + Ir * (RV::ONE_ROW ? RV::PITCH : 1024);
+        const int col = (rope ? C::VBYTES : 0) + 16 * c;
+        if (s >= 0)
+            __builtin_amdgcn_global_load_lds((const void*)(kvb + (int64_t)s * C::ROW_BYTES + col),
+                                             (lds_void*)dst, 16, 0, 0);
+    }
+    if (vmask != 0xffffffffu) {
+        for (int e = wv * kWave + lane; e < C::BUF / 16; e += C::THREADS) {
+            const int off = 16 * e;
+            const int r = off < RV::BYTES ? off / RV::PITCH : (off - RV::BYTES) / RR::PITCH;
+            if (!((vmask >> r) & 1u)) *(v4i*)(buf + off) = (v4i){0, 0, 0, 0};
+        }
+    }
+}
+
+template <int H, int DQK, int DV, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    int topk, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float2* __restrict__ part_ml, RowMap map, int n_rows, int n_split, float sm_log2) {
+    using C = MqaCfg<H, DQK, DV>;
+    using RV = typename C::RV;
+    using RR = typename C::RR;
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[C::BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[C::BUF];
+    __shared__ __attribute__((aligned(16))) float sx[2][2][4][kWave][4];  // [group][half][r/4][lane][r%4]
+
+    // Work item.  With two workgroups per row (64 heads each) the pair is issued 8 ids
+    // apart, i.e. onto the same XCD, so the second gather of each latent row hits its L2.
+    int row, hh;
+    if (C::NHH == 1) {
+        row = blockIdx.x;
+        hh = 0;
+    } else {
+        const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        row = (slot >> 1) * 8 + x;
+        hh = slot & 1;
+    }
+    if (row >= n_rows) return;
+    const int split = SPLIT ? blockIdx.y : 0;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int hg = wv & 1;  // head group: 32 heads
+    const int dp = wv >> 1;  // half: logit dims and value tiles
+    const RowInfo ri = row_info(map, row);
+    const int per = SPLIT ? (((topk + n_split - 1) / n_split + kBlk - 1) / kBlk) * kBlk : topk;
+    const int j0 = split * per;
+    const int j1 = min(topk, j0 + per);
+    const int nblk = j1 > j0 ? (j1 - j0 + kBlk - 1) / kBlk : 0;
+    const int32_t* irow = idx + (int64_t)row * topk;
+    const uint8_t* kvb = (const uint8_t*)(kv + (int64_t)ri.kbase * DQK);
+
+    // Query fragments of this wave's half of the dims: lane l holds head 64*hh + 32*hg + l%32,
+    // dims 16*ks + 8*(l/32) .. +7 for ks in [ks_begin, ks_begin + nks).
+    const int head = hh * 64 + hg * 32 + (lane & 31);
+    const int half = lane >> 5;
+    const int ks_begin = dp ? C::KS0 : 0;
+    const int nks = dp ? C::KS - C::KS0 : C::KS0;
+    v8bf qf[C::KS0];
+    {
+        const uint16_t* qp = q + ((int64_t)ri.qrow * H + (head < H ? head : 0)) * DQK + 8 * half;
+#pragma unroll
+        for (int i = 0; i < C::KS0; ++i) {
+            v4i v = {0, 0, 0, 0};
+            if (head < H && i < nks) v = *(const v4i*)(qp + 16 * (ks_begin + i));
+            qf[i] = __builtin_bit_cast(v8bf, v);
+        }
+    }
+
+    v16f oacc[C::VT0];
+#pragma unroll
+    for (int vt = 0; vt < C::VT0; ++vt) oacc[vt] = (v16f){};
+    float m_run = -INFINITY;  // running max of the base-2 logits of this lane's head
+    float l_run = 0.f;        // running sum over this lane's half of the block rows
+
+    // Block row held by MFMA row i = l%32 of the logit product: lanes of each 32-lane half
+    // must own 8 consecutive block rows per 16-row k-slice of the value product.
+    const int mi = lane & 31;
+    const int srow = 16 * (mi >> 4) + 8 * ((mi >> 2) & 1) + 4 * ((mi >> 3) & 1) + (mi & 3);
+    const int j16 = lane & 15;
+    const int vsub = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);  // value column of this tr16 lane
+
+    auto slot_index = [&](int blk) {
+        const int j = j0 + blk * kBlk + (lane & 31);
+        return j < j1 ? irow[j] : -1;
+    };
+
+    auto compute = [&](const uint8_t* base, int sidx) {
+        const uint64_t vmask = __ballot(sidx >= 0) & 0xffffffffull;
+        // ---- partial S^T = C Q^T over this wave's dims ----
+        v16f sacc = (v16f){};
+        v4i av[C::KS0];
+#pragma unroll
+        for (int i = 0; i < C::KS0; ++i) {  // operand loads first, so they overlap
+            const int ks = ks_begin + i;
+            const int off = ks < C::KSV ? RV::chunk(srow, 2 * ks + half)
+                                        : RV::BYTES + RR::chunk(srow, 2 * (ks - C::KSV) + half);
+            av[i] = i < nks ? *(const v4i*)(base + off) : (v4i){0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < C::KS0; ++i)
+            if (i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
+        // ---- sum the two halves: both waves of a group form S0 + S1 in the same order ----
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            *(v4f*)sx[hg][dp][r4][lane] =
+                (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2], sacc[4 * r4 + 3]};
+        lds_barrier();
+        float s[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const v4f a = *(const v4f*)sx[hg][0][r4][lane];
+            const v4f b = *(const v4f*)sx[hg][1][r4][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[4 * r4 + e] = a[e] + b[e];
+        }
+        if (vmask == 0ull) return;
+        // ---- online softmax: reg r <-> block row 16*(r/8) + 8*half + r%8 ----
+        float z[16];
+        float mb = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
+            const bool ok = (vmask >> slot) & 1ull;
+            z[r] = ok ? s[r] * sm_log2 : -INFINITY;
+            mb = fmaxf(mb, z[r]);
+        }
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const bool bump = mb > m_run + 8.f;
+        const bool fresh = m_run == -INFINITY;
+        if (__ballot(bump) != 0ull) {
+            const float m_new = bump ? mb : m_run;
+            const float alpha = fresh ? 0.f : exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            if (__ballot(!fresh) != 0ull) {
+#pragma unroll
+                for (int vt = 0; vt < C::VT0; ++vt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[vt][r] *= alpha;
+            }
+        }
+        v8bf pf[2];
+        float ls = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = exp2f(z[8 * u + e] - m_run);
+                ls += pv;
+                pf[u][e] = (__bf16)pv;
+            }
+        l_run += ls;
+        // ---- O^T += V^T P^T over this wave's value tiles ----
+        // tr16 source lane j of each 16-lane group points at block row 16u + 8*half + j/4
+        // (+4 for the second read), value columns vsub .. vsub+3 of the tile.
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int r_lo = 16 * u + 8 * half + (j16 >> 2);
+            v8bf va[C::VT0];
+#pragma unroll
+            for (int t = 0; t < C::VT0; ++t) {  // operand loads first, so they overlap
+                const int col = 32 * (dp * C::VT0 + t) + vsub;  // value column (bf16 index)
+                const int c = col >> 3, sub = (col & 7) * 2;
+                const v4s lo = ds_read_tr16(base + RV::chunk(r_lo, c) + sub);
+                const v4s hi = ds_read_tr16(base + RV::chunk(r_lo + 4, c) + sub);
+                const v2i l2 = __builtin_bit_cast(v2i, lo), h2 = __builtin_bit_cast(v2i, hi);
+                va[t] = __builtin_bit_cast(v8bf, (v4i){l2.x, l2.y, h2.x, h2.y});
+            }
+#pragma unroll
+            for (int t = 0; t < C::VT0; ++t) oacc[t] = mfma_bf16(va[t], pf[u], oacc[t]);
+        }
+    };
+
+    // Double-buffered sweep over the blocks: loads of block b+1 fly while block b computes.
+    int s_cur = nblk > 0 ? slot_index(0) : -1;
+    if (nblk > 0) gather_block<C>(lds0, kvb, s_cur, (uint32_t)__ballot(s_cur >= 0), wv, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int blk = 0; blk < nblk; blk += 2) {
+        const int s_nxt = blk + 1 < nblk ? slot_index(blk + 1) : -1;
+        if (blk + 1 < nblk) gather_block<C>(lds1, kvb, s_nxt, (uint32_t)__ballot(s_nxt >= 0), wv, lane);
+        compute(lds0, s_cur);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (blk + 1 >= nblk) break;
+        s_cur = blk + 2 < nblk ? slot_index(blk + 2) : -1;
+        if (blk + 2 < nblk) gather_block<C>(lds0, kvb, s_cur, (uint32_t)__ballot(s_cur >= 0), wv, lane);
+        compute(lds1, s_nxt);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    // ---- epilogue ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (head >= H) return;
+    if (!SPLIT) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* op = out + ((int64_t)ri.qrow * H + head) * DV;
+#pragma unroll
+        for (int t = 0; t < C::VT0; ++t)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int v = 32 * (dp * C::VT0 + t) + 8 * rb + 4 * half;
+                const uint32_t w0 = (uint32_t)f2bf(oacc[t][4 * rb + 0] * inv) |
+                                    ((uint32_t)f2bf(oacc[t][4 * rb + 1] * inv) << 16);
+                const uint32_t w1 = (uint32_t)f2bf(oacc[t][4 * rb + 2] * inv) |
+                                    ((uint32_t)f2bf(oacc[t][4 * rb + 3] * inv) << 16);
+                *(v2i*)(op + v) = (v2i){(int)w0, (int)w1};
+            }
+        if (lse != nullptr && half == 0 && dp == 0)
+            lse[(int64_t)ri.qrow * H + head] =
+                l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    } else {
+        const int64_t item = (int64_t)row * n_split + split;
+        float* op = part_o + (item * H + head) * DV;
+#pragma unroll
+        for (int t = 0; t < C::VT0; ++t)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int v = 32 * (dp * C::VT0 + t) + 8 * rb + 4 * half;
+                *(v4f*)(op + v) = (v4f){oacc[t][4 * rb + 0], oacc[t][4 * rb + 1],
+                                        oacc[t][4 * rb + 2], oacc[t][4 * rb + 3]};
+            }
+        if (half == 0 && dp == 0) part_ml[item * H + head] = make_float2(m_run, l_tot);
+    }
+}
+
+// Merges the split partials of each (row, head): weights 2^(m_j - M) on the unnormalised
+// partial outputs and sums.
+template <int H, int DV>
+__global__ __launch_bounds__(256) void mqa_combine_kernel(const float* __restrict__ part_o,
+                                                          const float2* __restrict__ part_ml,
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse, RowMap map,
+                                                          int n_rows, int n_split) {
+    const int row = blockIdx.x;
+    const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (row >= n_rows || head >= H) return;
+    const int lane = threadIdx.x & 63;
+    const RowInfo ri = row_info(map, row);
+    float M = -INFINITY;
+    for (int j = 0; j < n_split; ++j) M = fmaxf(M, part_ml[((int64_t)row * n_split + j) * H + head].x);
+    float L = 0.f;
+    float acc[DV / 64];
+#pragma unroll
+    for (int i = 0; i < DV / 64; ++i) acc[i] = 0.f;
+    if (M != -INFINITY) {
+        for (int j = 0; j < n_split; ++j) {
+            const int64_t item = (int64_t)row * n_split + j;
+            const float2 ml = part_ml[item * H + head];
+            if (ml.x == -INFINITY) continue;
+            const float wgt = exp2f(ml.x - M);
+            L += ml.y * wgt;
+            const float* op = part_o + (item * H + head) * DV;
+#pragma unroll
+            for (int i = 0; i < DV / 64; ++i) acc[i] += wgt * op[lane + 64 * i];
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* o = out + ((int64_t)ri.qrow * H + head) * DV;
+#pragma unroll
+    for (int i = 0; i < DV / 64; ++i) o[lane + 64 * i] = f2bf(acc[i] * inv);
+    if (lse != nullptr && lane == 0)
+        lse[(int64_t)ri.qrow * H + head] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+// Grid width: one workgroup per (row, 64-head half); rows are padded to a multiple of 8 when
+// a row has two halves so the XCD-pairing map stays in range (padding ids exit at once).
+template <class C>
+int grid_x(int n_rows) {
+    return C::NHH == 1 ? n_rows : ((n_rows + 7) / 8) * 8 * C::NHH;
+}
+
+template <int H, int DQK, int DV>
+hipError_t launch_t(const MqaArgs& a, const RowMap& map, int n_rows, int n_split, void* ws,
+                    hipStream_t st) {
+    using C = MqaCfg<H, DQK, DV>;
+    const float sm_log2 = a.sm_scale * 1.4426950408889634f;
+    if (n_split <= 1) {
+        hipLaunchKernelGGL((sparse_mqa_kernel<H, DQK, DV, false>), dim3(grid_x<C>(n_rows)), dim3(C::THREADS), 0,
+                           st, a.q, a.kv, a.idx, a.topk, a.out, a.lse, nullptr, nullptr, map, n_rows,
+                           1, sm_log2);
+        return hipGetLastError();
+    }
+    float* part_o = (float*)ws;
+    float2* part_ml = (float2*)(part_o + (size_t)n_rows * n_split * H * DV);
+    hipLaunchKernelGGL((sparse_mqa_kernel<H, DQK, DV, true>), dim3(grid_x<C>(n_rows), n_split), dim3(C::THREADS),
+                       0, st, a.q, a.kv, a.idx, a.topk, a.out, a.lse, part_o, part_ml, map, n_rows,
+                       n_split, sm_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mqa_combine_kernel<H, DV>), dim3(n_rows, (H + 3) / 4), dim3(256), 0, st,
+                       part_o, part_ml, a.out, a.lse, map, n_rows, n_split);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t mqa_split_bytes(Shape shape, int n_rows, int n_split) {
+    if (n_split <= 1) return 0;
+    const size_t H = shape == Shape::Prod ? 128 : 8;
+    const size_t DV = shape == Shape::Prod ? 512 : 64;
+    return (size_t)n_rows * n_split * H * (DV * sizeof(float) + sizeof(float2));
+}
+
+hipError_t launch_sparse_mqa(const MqaArgs& a, const RowMap& map, int n_rows, int n_split,
+                             void* ws, hipStream_t st) {
+    if (n_rows <= 0) return hipSuccess;
+    if (a.shape == Shape::Prod) return launch_t<128, 576, 512>(a, map, n_rows, n_split, ws, st);
+    return launch_t<8, 80, 64>(a, map, n_rows, n_split, ws, st);
+}
+
+}  // namespace dsa

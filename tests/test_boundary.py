@@ -1,0 +1,127 @@
+"""The C-ABI boundary on the host: the library loads, exports every function declared in
+include/dsa.h, and rejects invalid arguments with the documented status before enqueueing
+anything (these calls never touch device memory, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_attention_long_lightning_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 1 << 20  # 16-byte aligned address; never dereferenced on the error paths below
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_mqa", "dsa_forward",
+            "dsa_workspace_size", "dsa_status_string"} <= set(names)
+    lib = dsa.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = dsa.lib()
+    for s, name in dsa.STATUS.items():
+        assert lib.dsa_status_string(s).decode().startswith(name)
+
+
+def cpu_batch(cu_q, cu_k):
+    return dsa.Batch(cu_q, cu_k, device="cpu")
+
+
+def call_forward(dims, batch, ptr=FAKE, ws_bytes=1 << 40, **over):
+    args = dict(q8=ptr, q_scale=ptr, w=ptr, k8=ptr, k_scale=ptr, q=ptr, kv=ptr, out=ptr, lse=None,
+                idx=None, ws=ptr)
+    args.update(over)
+    return dsa.lib().dsa_forward(ctypes.byref(dims), ctypes.byref(batch.c), args["q8"],
+                                 args["q_scale"], args["w"], args["k8"], args["k_scale"], args["q"],
+                                 args["kv"], args["out"], args["lse"], args["idx"], args["ws"],
+                                 ws_bytes, None)
+
+
+def dims_with(**kw):
+    d = dsa.Dims(64, 128, 2048, 128, 576, 512, 0.0721)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(topk=0), INVALID), (dict(topk=2049), INVALID), (dict(topk=-5), INVALID),
+    (dict(sm_scale=0.0), INVALID), (dict(sm_scale=float("nan")), INVALID),
+    (dict(sm_scale=float("inf")), INVALID), (dict(n_idx_heads=32), UNSUPPORTED),
+    (dict(idx_dim=64), UNSUPPORTED), (dict(n_heads=64), UNSUPPORTED), (dict(qk_dim=512), UNSUPPORTED),
+    (dict(v_dim=576), UNSUPPORTED)])
+def test_invalid_dims(kw, status):
+    b = cpu_batch([0, 4096], [0, 4096])
+    assert call_forward(dims_with(**kw), b) == status
+    out = ctypes.c_size_t(0)
+    assert dsa.lib().dsa_workspace_size(ctypes.byref(dims_with(**kw)), ctypes.byref(b.c),
+                                        ctypes.byref(out)) == status
+
+
+@pytest.mark.parametrize("cu_q,cu_k", [
+    ([1, 4], [0, 4]),          # not zero-based
+    ([0, 4], [1, 4]),
+    ([0, 8], [0, 4]),          # more queries than keys
+    ([0, 4, 2], [0, 4, 8]),    # decreasing offsets
+    ([0, 2, 4], [0, 8, 6])])
+def test_invalid_batches(cu_q, cu_k):
+    assert call_forward(dims_with(), cpu_batch(cu_q, cu_k)) == INVALID
+
+
+def test_null_and_misaligned_pointers():
+    d, b = dims_with(), cpu_batch([0, 64], [0, 64])
+    for name in ("q8", "q_scale", "w", "k8", "k_scale", "q", "kv", "out"):
+        assert call_forward(d, b, **{name: None}) == INVALID, name
+        assert call_forward(d, b, **{name: FAKE + 4}) == INVALID, name
+    assert call_forward(d, b, lse=FAKE + 8) == INVALID
+    assert call_forward(d, b, idx=FAKE + 2) == INVALID
+    assert call_forward(d, b, ws=None) == WORKSPACE
+    lib = dsa.lib()
+    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 64, None, None) == INVALID
+    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 60, FAKE, None) == INVALID  # stride < len
+    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 66, FAKE, None) == INVALID  # not x4
+    assert lib.dsa_indexer_scores(ctypes.byref(d), ctypes.byref(b.c), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE + 4, 64, None) == INVALID
+    assert lib.dsa_sparse_mqa(ctypes.byref(d), ctypes.byref(b.c), FAKE, FAKE, None, FAKE, None, None,
+                              0, None) == INVALID
+
+
+def test_workspace_too_small_is_rejected():
+    d, b = dims_with(), cpu_batch([0, 4096], [0, 4096])
+    lo = dsa.workspace_min(d, b)
+    hi = dsa.workspace_size(d, b)
+    assert 0 < lo <= hi
+    assert call_forward(d, b, ws_bytes=lo - 1) == WORKSPACE
+    # decode batches need the split partials of the attention as well
+    db = cpu_batch(list(range(33)), [i * 40000 for i in range(33)])
+    assert call_forward(d, db, ws_bytes=dsa.workspace_size(d, db) - 1) == WORKSPACE
+    assert dsa.lib().dsa_sparse_mqa(ctypes.byref(d), ctypes.byref(db.c), FAKE, FAKE, FAKE, FAKE, None,
+                                    FAKE, 16, None) == WORKSPACE
+
+
+def test_workspace_policy_is_bounded_by_chunking():
+    d = dims_with()
+    b128 = cpu_batch([0, 131072], [0, 131072])
+    ws = dsa.workspace_size(d, b128)
+    # one pass of 8192 query rows of fp32 scores (+ their index rows), never the full L x L
+    assert ws < 131072 * 131072 * 4 / 8
+    assert ws >= 8192 * 131072 * 4
+
+
+def test_empty_batch_is_a_no_op():
+    d = dims_with()
+    b = cpu_batch([0, 0], [0, 100])
+    assert call_forward(d, b, ptr=None, ws_bytes=0) == OK
