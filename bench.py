@@ -1,0 +1,291 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+A step is one dsa_forward over the whole workload (lightning indexer -> top-k -> sparse MQA)
+with every input already resident in HBM.  Default workload: causal prefill of one
+131072-token sequence (k = 2048, 64 FP8 indexer heads of dim 128, 128 MQA heads over the
+576-wide latent cache).  Prints one JSON line.
+
+Besides the end-to-end rate the line carries:
+  stages        per-stage time of the same launches (each stage entry point called on the
+                same row passes as dsa_forward makes), measured with HIP events on the stream
+                the kernels run on, and each stage's algorithmic rate;
+  roofline      the dominant stage's achieved rate against its MI355X peak;
+  decode        batched decode (32 sequences, lengths uniform in [32768, 131072]);
+  cpu_baseline  the CPU oracle on a bounded, uniformly spaced sample of query rows of the
+                same workload, timed on the host (rank 0 only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import dsa_inputs  # noqa: E402
+import sparse_attention_long_lightning_amd as dsa  # noqa: E402
+
+METRIC = "DSA prefill tokens/s at 128K (+ indexer FP8 TFLOP/s); decode µs/token"
+PEAK = {"fp8": 5000.0, "bf16": 2500.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s (MI355X)
+FLOP_INDEXER_PAIR = 2 * 64 * 128       # per causal (query, key) pair
+FLOP_MQA_PAIR = 2 * 128 * (576 + 512)  # per selected (query, key) pair
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP-event timing on torch's current stream (the stream the library launches on)."""
+
+    def __init__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+
+    def ms(self):
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def prefill_case(L, dev):
+    dims = dsa_inputs.PROD
+    t0 = time.time()
+    inp = dsa_inputs.prefill_inputs(L, dims, seed=0, device=dev)
+    torch.cuda.synchronize()
+    log(f"generated prefill L={L} inputs in {time.time() - t0:.1f}s")
+    batch = dsa.Batch(inp["cu_q"], inp["cu_k"], device=dev)
+    out = torch.empty(L, dims.n_heads, dims.v_dim, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(L, dims.n_heads, dtype=torch.float32, device=dev)
+    ws = torch.empty(dsa.workspace_size(dims, batch), dtype=torch.uint8, device=dev)
+    return dict(dims=dims, inp=inp, batch=batch, out=out, lse=lse, ws=ws, L=L)
+
+
+def run_forward(c):
+    i = c["inp"]
+    dsa.forward(c["dims"], c["batch"], i["q8"], i["q_scale"], i["w"], i["k8"], i["k_scale"], i["q"],
+                i["kv"], c["out"], c["lse"], None, c["ws"])
+
+
+def chunk_rows(c):
+    """Row passes of dsa_forward at the default workspace: 8192 rows each."""
+    L = c["L"]
+    ch = min(8192, L)
+    return [(r0, min(L, r0 + ch)) for r0 in range(0, L, ch)]
+
+
+def stage_breakdown(c, reps=1):
+    """Runs the three stage entry points on the same row passes dsa_forward makes and times
+    every launch with HIP events.  Returns per-stage totals (ms) and algorithmic work."""
+    dims, inp, L = c["dims"], c["inp"], c["L"]
+    k = dims.topk
+    dev = inp["q8"].device
+    passes = chunk_rows(c)
+    ch = passes[0][1] - passes[0][0]
+    stride = (L + 3) // 4 * 4
+    scores = c["ws"][: ch * stride * 4].view(torch.float32).view(ch, stride)
+    idx = torch.empty(ch, k, dtype=torch.int32, device=dev)
+    t = {"indexer": 0.0, "topk": 0.0, "mqa": 0.0}
+    launches = {"indexer": 0, "topk": 0, "mqa": 0}
+    pairs_idx = 0
+    pairs_mqa = 0
+    for _ in range(reps):
+        for r0, r1 in passes:
+            n = r1 - r0
+            # the pass as its own batch: queries r0..r1-1 are the last n of keys 0..r1-1
+            b = dsa.Batch([0, n], [0, r1], device=dev)
+            rsel = max(r0, k)  # rows with p + 1 <= k need no scores
+            if rsel < r1:
+                bs = dsa.Batch([0, r1 - rsel], [0, r1], device=dev)
+                with Timer() as tm:
+                    dsa.indexer_scores(dims, bs, inp["q8"][rsel:], inp["q_scale"][rsel:], inp["w"][rsel:],
+                                       inp["k8"], inp["k_scale"], scores[rsel - r0:], stride)
+                t["indexer"] += tm.ms()
+                launches["indexer"] += 1
+                pairs_idx += sum_range(rsel + 1, r1)
+            with Timer() as tm:
+                dsa.topk(dims, b, scores, stride, idx)
+            t["topk"] += tm.ms()
+            launches["topk"] += 1
+            with Timer() as tm:
+                dsa.sparse_mqa(dims, b, inp["q"][r0:r1], inp["kv"], idx, c["out"][r0:r1], c["lse"][r0:r1],
+                               c["ws"])
+            t["mqa"] += tm.ms()
+            launches["mqa"] += 1
+            pairs_mqa += sum(min(p + 1, k) for p in range(r0, r1))
+    for s in t:
+        t[s] /= reps
+    pairs_idx //= reps
+    pairs_mqa //= reps
+    topk_rows = sum(1 for p in range(L) if p + 1 > k)
+    topk_bytes = 4 * pairs_idx + 8 * 1024 * L  # one read of every valid score + the index rows
+    return t, launches, dict(indexer_pairs=pairs_idx, mqa_pairs=pairs_mqa, topk_rows=topk_rows,
+                             topk_bytes=topk_bytes)
+
+
+def sum_range(lo, hi):
+    """Sum of the integers lo..hi (inclusive)."""
+    return (lo + hi) * (hi - lo + 1) // 2 if hi >= lo else 0
+
+
+def decode_case(dev, steps):
+    dims = dsa_inputs.PROD
+    inp = dsa_inputs.decode_inputs(32, dims, seed=0, device=dev)
+    batch = dsa.Batch(inp["cu_q"], inp["cu_k"], device=dev)
+    B = 32
+    out = torch.empty(B, dims.n_heads, dims.v_dim, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, dims.n_heads, dtype=torch.float32, device=dev)
+    ws = torch.empty(dsa.workspace_size(dims, batch), dtype=torch.uint8, device=dev)
+
+    def step():
+        dsa.forward(dims, batch, inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"],
+                    inp["q"], inp["kv"], out, lse, None, ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    with Timer() as tm:
+        for _ in range(steps):
+            step()
+    us = tm.ms() * 1e3 / steps
+    nkeys = int(inp["cu_k"][-1])
+    return dict(us_per_step=round(us, 2), us_per_token=round(us / B, 3), batch=B,
+                mean_context=round(nkeys / B), hbm_floor_mb=round((nkeys * 132 + B * 2048 * 1152) / 1e6, 1))
+
+
+def cpu_baseline(c, budget_s=20.0, max_rows=64):
+    """The oracle on uniformly spaced query rows of the same prefill (indexer over every
+    earlier key, top-k, MQA).  Rows are processed in growing batches until ~budget_s."""
+    import oracle
+
+    inp, L = c["inp"], c["L"]
+    host = {"cu_q": inp["cu_q"], "cu_k": inp["cu_k"], "dims": inp["dims"],
+            "k8": inp["k8"].cpu().numpy(), "k_scale": inp["k_scale"].cpu().numpy(),
+            "kv": inp["kv"].view(torch.int16).cpu().numpy().view(np.uint16)}
+    done = 0
+    spent = 0.0
+    n = oracle.num_threads()
+    rng = np.random.default_rng(0)
+    while spent < budget_s and done < max_rows:
+        m = min(max_rows - done, max(1, n))
+        rows = np.sort(rng.integers(0, L, m))
+        # only the sampled rows of the query side are copied to the host
+        rq = torch.from_numpy(rows).to(inp["q8"].device)
+        q8 = inp["q8"][rq].cpu().numpy()
+        qs = inp["q_scale"][rq].cpu().numpy()
+        w = inp["w"][rq].cpu().numpy()
+        q = inp["q"][rq].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        scores = oracle.indexer_rows(q8, qs, w, host["k8"], host["k_scale"], np.arange(m), rows)
+        sel = oracle.topk_rows(scores, inp["dims"].topk)
+        oracle.sparse_mqa(q, host["kv"], sel, inp["dims"].v_dim, inp["dims"].sm_scale)
+        spent += time.perf_counter() - t0
+        done += m
+    return dict(value=round(done / spent, 3), unit="tokens/s", cores=n, kind="oracle",
+                sample=f"{done} query rows drawn uniformly from the L={L} prefill (positions "
+                       f"seeded), each through the oracle's indexer over all earlier keys, "
+                       f"top-k and sparse MQA; {spent:.1f}s of host time")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--seq-len", type=int, default=131072)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    L = args.seq_len
+    c = prefill_case(L, dev)
+    log(f"workspace {c['ws'].numel() / 2**30:.2f} GiB")
+    for _ in range(args.warmup):
+        run_forward(c)
+    torch.cuda.synchronize()
+    log("timed region")
+    with Timer() as tm:
+        for _ in range(args.steps):
+            run_forward(c)
+    torch.cuda.synchronize()
+    ms = tm.ms() / args.steps
+    tok_s = L / (ms / 1e3)
+    log(f"prefill L={L}: {ms:.2f} ms/step, {tok_s:,.0f} tokens/s")
+
+    line = {"metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8-e4m3 indexer + bf16 attention (fp32 accumulate)", "data": "synthetic",
+            "config": {"workload": f"DSA causal prefill, one sequence L={L}, k=2048, indexer 64 heads x 128 "
+                                   f"(FP8 e4m3), MQA 128 heads over a 576-wide bf16 latent cache (value 512), "
+                                   f"64 planted needles per 4K block, seed 0",
+                       "seq_len": L, "topk": 2048, "global_batch": 1}}
+    if not args.no_stages:
+        t, launches, work = stage_breakdown(c)
+        stages = {}
+        tf_idx = work["indexer_pairs"] * FLOP_INDEXER_PAIR / (t["indexer"] / 1e3) / 1e12
+        tf_mqa = work["mqa_pairs"] * FLOP_MQA_PAIR / (t["mqa"] / 1e3) / 1e12
+        gb_topk = work["topk_bytes"] / (t["topk"] / 1e3) / 1e9
+        stages["indexer"] = dict(ms=round(t["indexer"], 3), launches=launches["indexer"],
+                                 tflops=round(tf_idx, 1), frac_fp8_peak=round(tf_idx / PEAK["fp8"], 4),
+                                 tokens_per_s=round(L / (t["indexer"] / 1e3), 1))
+        stages["topk"] = dict(ms=round(t["topk"], 3), launches=launches["topk"], gbps=round(gb_topk, 1),
+                              frac_hbm_peak=round(gb_topk / PEAK["hbm"], 4),
+                              tokens_per_s=round(L / (t["topk"] / 1e3), 1))
+        stages["mqa"] = dict(ms=round(t["mqa"], 3), launches=launches["mqa"], tflops=round(tf_mqa, 1),
+                             frac_bf16_peak=round(tf_mqa / PEAK["bf16"], 4),
+                             tokens_per_s=round(L / (t["mqa"] / 1e3), 1))
+        line["stages"] = stages
+        line["indexer_fp8_tflops"] = round(tf_idx, 1)
+        dom = max(t, key=lambda s: t[s])
+        if dom == "indexer":
+            per = work["indexer_pairs"] * FLOP_INDEXER_PAIR / launches["indexer"] / 1e12
+            avg = t["indexer"] / launches["indexer"] / 1e3
+            roof = dict(kernel="indexer_prefill_kernel", bound="mfma", achieved=round(per / avg, 1),
+                        peak=PEAK["fp8"], unit="TFLOP/s")
+        elif dom == "mqa":
+            per = work["mqa_pairs"] * FLOP_MQA_PAIR / launches["mqa"] / 1e12
+            avg = t["mqa"] / launches["mqa"] / 1e3
+            roof = dict(kernel="sparse_mqa_kernel", bound="mfma", achieved=round(per / avg, 1),
+                        peak=PEAK["bf16"], unit="TFLOP/s")
+        else:
+            per = work["topk_bytes"] / launches["topk"] / 1e9
+            avg = t["topk"] / launches["topk"] / 1e3
+            roof = dict(kernel="topk_kernel", bound="hbm", achieved=round(per / avg, 1),
+                        peak=PEAK["hbm"], unit="GB/s")
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        roof["traffic"] = None
+        roof["avg_launch_ms"] = round(avg * 1e3, 3)
+        line["roofline"] = roof
+        log(f"stages {json.dumps(stages)}")
+    if not args.no_decode:
+        del c["out"]
+        torch.cuda.empty_cache()
+        line["decode"] = decode_case(dev, steps=20)
+        log(f"decode {line['decode']}")
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c)
+        log(f"cpu baseline {line['cpu_baseline']}")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -112,10 +112,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void indexer_prefill_kernel(
     if (tmax < k0) return;
     const int ngroups = (min(kend, tmax + 1) - k0 + 15) >> 4;
     for (int g = 0; g < ngroups; ++g) {
-        const uint8_t* bp = lk + (16 * g + col) * KPITCH + grp * 32;
-        const v4i blo = *(const v4i*)bp;
-        const v4i bhi = *(const v4i*)(bp + 16);
-        const v8i b = {blo.x, blo.y, blo.z, blo.w, bhi.x, bhi.y, bhi.z, bhi.w};
+        // k-groups past the head dim carry zeros in A and must carry zeros in B as well:
+        // 0 * (a stray NaN code) would poison the whole column.
+        v8i b = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (grp < KGRP) {
+            const uint8_t* bp = lk + (16 * g + col) * KPITCH + grp * 32;
+            const v4i blo = *(const v4i*)bp;
+            const v4i bhi = *(const v4i*)(bp + 16);
+            b = (v8i){blo.x, blo.y, blo.z, blo.w, bhi.x, bhi.y, bhi.z, bhi.w};
+        }
         v4f acc[2][NMT];
 #pragma unroll
         for (int tok = 0; tok < 2; ++tok)

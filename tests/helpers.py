@@ -34,13 +34,23 @@ def check_attention(got_bits: np.ndarray, ref: np.ndarray, max_abs=2e-2, rel=1e-
     return m, r
 
 
-def check_scores(got: np.ndarray, ref: np.ndarray, mag: np.ndarray, tol=1e-3, what=""):
-    """Indexer parity: |g - o| <= tol * M, M = s_k * sum_j |w'_j| ReLU(D_j) (computed by the
-    oracle as the score with |w| in place of w), plus a few fp32 ulps of M for M ~ 0."""
-    bound = tol * mag + 4 * np.finfo(np.float32).eps * mag + 1e-30
-    bad = np.abs(got.astype(np.float64) - ref) > bound
-    assert not bad.any(), (f"{what}: {int(bad.sum())} scores out of tolerance; worst at "
-                           f"{np.unravel_index(np.argmax(np.abs(got - ref) - bound), got.shape)}")
+def check_scores(got: np.ndarray, ref: np.ndarray, mag: np.ndarray, mag_abs: np.ndarray,
+                 tol=1e-3, eps_acc=2.0 ** -14, what=""):
+    """Indexer parity: |g - o| <= tol * M + eps_acc * A, where
+    M = s_k sum_j |w'_j| ReLU(D_j)           (the oracle's score with |w| in place of w) and
+    A = s_k sum_j |w'_j| sum_d |q_jd k_d|    (the score with |w| and sign-free codes).
+    The second term bounds the accumulation error of the gfx950 FP8 MFMA, which does not sum
+    the (exact) products in full fp32: measured on operands quantised like the workload, its
+    error stays below 2^-16.5 of the summed product magnitudes; eps_acc = 2^-14 allows 4x that.
+    It only matters where the head dot products D_j cancel to nearly nothing, which a bound
+    relative to M alone cannot cover."""
+    bound = tol * mag + eps_acc * mag_abs + 1e-30
+    diff = np.abs(got.astype(np.float64) - ref)
+    bad = diff > bound
+    if bad.any():
+        i = int(np.argmax(diff - bound))
+        raise AssertionError(f"{what}: {int(bad.sum())} scores out of tolerance; worst at {i}: "
+                             f"gpu {got[i]!r} oracle {ref[i]!r} M {mag[i]!r} A {mag_abs[i]!r}")
 
 
 def check_sets(gpu_idx: np.ndarray, orc_idx: np.ndarray, orc_scores: np.ndarray, k: int, tol=1e-3):

@@ -37,25 +37,31 @@ def run_indexer(inp, dims, dev, rows=None):
     return scores
 
 
-def oracle_scores(h, rows, seq=0, absw=False):
+def oracle_scores(h, rows, seq=0, mode="score"):
+    """The oracle's scores; mode "absw" uses |w| (magnitude M), mode "abs" uses |w| and the
+    codes with their sign bits cleared (magnitude A of the summed products)."""
     cu_q, cu_k = h["cu_q"], h["cu_k"]
     q0, q1, k0, k1 = cu_q[seq], cu_q[seq + 1], cu_k[seq], cu_k[seq + 1]
     rows = np.asarray(rows)
     pos = (k1 - k0) - (q1 - q0) + rows
-    w = np.abs(h["w"]) if absw else h["w"]
-    return oracle.indexer_rows(h["q8"][q0 + rows], h["q_scale"][q0 + rows], w[q0 + rows],
-                               h["k8"][k0:k1], h["k_scale"][k0:k1], np.arange(len(rows)), pos)
+    w = np.abs(h["w"]) if mode != "score" else h["w"]
+    q8, k8 = h["q8"], h["k8"]
+    if mode == "abs":
+        q8, k8 = q8 & np.uint8(0x7F), k8 & np.uint8(0x7F)
+    return oracle.indexer_rows(q8[q0 + rows], h["q_scale"][q0 + rows], w[q0 + rows],
+                               k8[k0:k1], h["k_scale"][k0:k1], np.arange(len(rows)), pos)
 
 
 def compare_indexer_rows(scores, h, rows, what, seq=0):
     ref = oracle_scores(h, rows, seq)
-    mag = oracle_scores(h, rows, seq, absw=True)
+    mag = oracle_scores(h, rows, seq, mode="absw")
+    mag_abs = oracle_scores(h, rows, seq, mode="abs")
     base = h["cu_q"][seq]
     for i, r in enumerate(rows):
         n = len(ref[i])
         got = scores[base + r, :n]
         assert np.isfinite(got).all(), f"{what}: row {r} has unwritten entries"
-        check_scores(got, ref[i], mag[i], what=f"{what} row {r}")
+        check_scores(got, ref[i], mag[i], mag_abs[i], what=f"{what} row {r}")
 
 
 # ------------------------------------------------------------------ indexer ---------------
