@@ -5,19 +5,24 @@
 // rope; every head shares the row):
 //     z_s = sm * <q[t,h,:], c_s>,  out[t,h,:] = sum_s softmax(z)_s c_s[:512],  lse = ln sum e^z
 //
-// One workgroup owns one query row and all its heads: wave w owns heads 32w..32w+31, so each
-// gathered latent row is staged in LDS once and reused by every head.  Per block of 32
-// selected rows:
-//   S^T = C Q^T   v_mfma_f32_32x32x16_bf16, A = latent rows from LDS (M = 32 rows),
-//                 B = the wave's 32 query heads kept in registers for the whole row (N = heads)
-//   online softmax in base 2 on S^T: lane l owns head l%32, so the running max / sum are
-//                 per-lane values (one exchange with lane l^32 per block)
-//   O^T += V^T P^T   A = value columns read from the same row-major LDS block with the
-//                 gfx950 transpose read (ds_read_b64_tr_b16), B = P^T straight from the S^T
-//                 accumulators (row order of S^T is chosen so that each lane already holds
-//                 8 consecutive rows per MFMA k-slice).
-// Rescaling of O is lazy: the running max only moves when a block's max exceeds it by more
-// than 8 (factor 256 of headroom in fp32), which keeps the arithmetic exact up to rounding.
+// Work decomposition: one workgroup = one query row x 64 heads (two workgroups per row of 128
+// heads, issued 8 ids apart so both run on the same XCD and the second gather of each latent
+// row hits its L2).  Its 4 waves are 2 head groups (32 heads) x 2 halves; a half owns half of
+// the 576 logit dims (query fragments stay in registers) and half of the 512 value dims
+// (fp32 accumulators).  Per block of 32 selected rows:
+//   gather   direct global->LDS loads (no staging registers) in a three-deep ring, so the
+//            loads of the next two blocks fly while this one computes;
+//   S^T      = C Q^T with v_mfma_f32_32x32x16_bf16 (A = latent rows from LDS, M = rows;
+//            B = query heads, N = heads) over the wave's dims; the halves' partial tiles are
+//            summed through LDS (both waves form S0 + S1 in the same order);
+//   softmax  online, in base 2; lane l owns head l%32, so running max and sum are per lane
+//            (one exchange with lane l^32); O is rescaled only when a block max exceeds the
+//            running max by more than 16 (2^16 of headroom in fp32 and bf16 P);
+//   O^T      += V^T P^T with A = value columns read by ds_read_b64_tr_b16 straight from the
+//            row-major block and B = P^T taken from the S^T accumulators (the S^T row order
+//            puts 8 consecutive block rows in each lane per 16-row k-slice).
+// LDS rows are XOR-swizzled in 16-byte chunks so that the 16 rows read together by an A
+// operand, and the 4 consecutive rows of a transpose read, fall in distinct bank groups.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -25,26 +30,24 @@ namespace dsa {
 
 namespace {
 
-constexpr int kBlk = 32;  // selected rows per LDS block
+constexpr int kBlk = 32;            // selected rows per LDS block
+constexpr float kRescaleGap = 16.f;  // base-2 headroom before O is rescaled
 
-// LDS image of one block of kBlk latent rows, split in two regions of 16-byte chunks:
-// the value part (first DV columns) and the rope part (the remaining DQK - DV columns).
-// Rows are written by direct global->LDS loads, 64 chunks (1 KiB) per wave instruction:
-//  - a region with 64 chunks per row gets one row per instruction and a 16-byte pad per row,
-//  - a narrower region packs 64/NC rows per instruction and XOR-swizzles the chunk index
-//    of each row instead, so rows read together by one MFMA operand land in different banks.
+// One region (value part or rope part) of the LDS image of a block: kBlk rows of NC 16-byte
+// chunks, written 1 KiB (64 chunks) per direct-load instruction.
 template <int NC>
 struct Region {
-    static constexpr bool ONE_ROW = NC == 64;
+    static_assert(NC == 64 || NC == 8 || NC == 2, "unsupported region width");
     static constexpr int ROWS_PER_INSTR = 64 / NC;
-    static constexpr int PITCH = ONE_ROW ? NC * 16 + 16 : NC * 16;
+    static constexpr int PITCH = NC * 16;
     static constexpr int BYTES = kBlk * PITCH;
     static constexpr int INSTRS = kBlk / ROWS_PER_INSTR;
-    static_assert(NC == 64 || NC == 8 || NC == 2, "unsupported region width");
+    // 64-chunk rows: any 16 consecutive rows and any 4 consecutive rows (x 4 chunks) map to
+    // distinct 16-byte bank groups; narrow rows: pairs of rows share a 256-byte line.
     __device__ static __forceinline__ int swz(int r) {
-        return ONE_ROW ? 0 : (((r & 3) | ((r & 8) >> 1)) & (NC - 1));
+        if constexpr (NC == 64) return ((r & 3) << 2) | ((r >> 2) & 3);
+        else return (r >> 1) & (NC - 1);
     }
-    // byte offset of logical chunk c of row r
     __device__ static __forceinline__ int chunk(int r, int c) { return r * PITCH + 16 * (c ^ swz(r)); }
 };
 
@@ -62,8 +65,11 @@ struct MqaCfg {
     using RR = Region<(DQK - DV) * 2 / 16>;
     static constexpr int BUF = RV::BYTES + RR::BYTES;
     static constexpr int INSTRS = RV::INSTRS + RR::INSTRS;
-    static constexpr int ROW_BYTES = DQK * 2;  // bytes of one latent row in memory
-    static constexpr int VBYTES = DV * 2;      // bytes of its value part
+    static constexpr int ROW_BYTES = DQK * 2;           // bytes of one latent row in memory
+    static constexpr int VBYTES = DV * 2;               // bytes of its value part
+    static constexpr int LOADS_PER_WAVE = INSTRS / NW;  // direct loads per wave and block (min)
+    static constexpr bool EVEN = KS % 2 == 0;           // both halves have KS0 slices
+    static constexpr int QK_AHEAD = KS0 < 9 ? KS0 : 9;  // logit operand loads kept in flight
     static_assert(DQK % 16 == 0 && DV % 64 == 0, "unsupported latent widths");
     static_assert(NHH <= 2, "at most 128 heads");
 };
@@ -80,11 +86,36 @@ __device__ __forceinline__ v4s ds_read_tr16(const uint8_t* p) {
 }
 
 // Workgroup barrier that orders LDS accesses only: in-flight direct global->LDS loads into
-// the other buffer are not waited for (the fence of a full __syncthreads would drain them).
+// the other buffers are not waited for (the fence of a full __syncthreads would drain them).
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // no LDS access moves above the barrier
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Reads the two halves' partial logit tiles (4 x 16 bytes each, 1 KiB apart) and waits for
+// them inside the same asm block.  Written as asm so that the compiler does not treat these
+// LDS reads as possibly aliasing the in-flight direct loads of later blocks (it would drain
+// them with a vmcnt(0) wait); nothing is left in flight when the block ends.
+__device__ __forceinline__ void read_partials(uint32_t a0, uint32_t b0, v4f a[4], v4f b[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %8 offset:1024\n"
+        "ds_read_b128 %2, %8 offset:2048\n"
+        "ds_read_b128 %3, %8 offset:3072\n"
+        "ds_read_b128 %4, %9\n"
+        "ds_read_b128 %5, %9 offset:1024\n"
+        "ds_read_b128 %6, %9 offset:2048\n"
+        "ds_read_b128 %7, %9 offset:3072\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]),
+          "=&v"(b[3])
+        : "v"(a0), "v"(b0)
+        : "memory");
 }
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -92,38 +123,61 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
-// Issues the direct loads of one block into the LDS image at `buf`: lane l%32 holds the
-// latent row index of block row l%32 in `sidx` (-1 for an empty slot) and bit r of `vmask`
-// tells whether block row r is occupied.  Empty rows are zero-filled so that they contribute
-// exact zeros to both products.
+// Row and LDS byte offset of the 16-byte piece that lane `lane` moves in direct-load
+// instruction I of a block (the hardware adds 16 * lane to the instruction's LDS base), and
+// the byte column of the latent row it fetches.
 template <class C>
-__device__ __forceinline__ void gather_block(uint8_t* buf, const uint8_t* kvb, int sidx,
-                                             uint32_t vmask, int wv, int lane) {
+__device__ __forceinline__ void piece_of(int I, int lane, int& r, int& col, int& base) {
     using RV = typename C::RV;
     using RR = typename C::RR;
+    const bool rope = I >= RV::INSTRS;
+    const int Ir = rope ? I - RV::INSTRS : I;
+    const int rows = rope ? RR::ROWS_PER_INSTR : RV::ROWS_PER_INSTR;
+    const int ncol = 64 / rows;  // chunks per row in this region
+    r = Ir * rows + lane / ncol;
+    const int p = lane % ncol;
+    const int c = rope ? (p ^ RR::swz(r)) : (p ^ RV::swz(r));
+    col = (rope ? C::VBYTES : 0) + 16 * c;
+    base = rope ? RV::BYTES + Ir * 1024 : Ir * 1024;
+}
+
+// Issues the direct global->LDS loads of one block of kBlk latent rows into `buf`.  Lane l%32
+// holds the row index of block row l%32 in `sidx` (-1 = empty slot).  Every wave issues the
+// same number of instructions for every block (empty slots load row 0 of the sequence and are
+// zeroed by zero_empty_rows once they have landed), so the wait can count them.
+template <class C>
+__device__ __forceinline__ void issue_block(uint8_t* buf, const uint8_t* kvb, int sidx, int wv,
+                                            int lane) {
     for (int I = wv; I < C::INSTRS; I += C::NW) {  // same trip count on every lane
-        const bool rope = I >= RV::INSTRS;
-        const int Ir = rope ? I - RV::INSTRS : I;
-        const int rows = rope ? RR::ROWS_PER_INSTR : RV::ROWS_PER_INSTR;
-        const int ncol = 64 / rows;  // chunks per row in this region
-        const int r = Ir * rows + lane / ncol;
-        const int p = lane % ncol;
-        const int c = rope ? (p ^ RR::swz(r)) : (p ^ RV::swz(r));
-        const int s = __shfl(sidx, r);
-        uint8_t* dst = rope ? buf + RV::BYTES + Ir * (RR::ONE_ROW ? RR::PITCH : 1024)
-                            : buf + Ir * (RV::ONE_ROW ? RV::PITCH : 1024);
-        const int col = (rope ? C::VBYTES : 0) + 16 * c;
-        if (s >= 0)
-            __builtin_amdgcn_global_load_lds((const void*)(kvb + (int64_t)s * C::ROW_BYTES + col),
-                                             (lds_void*)dst, 16, 0, 0);
+        int r, col, base;
+        piece_of<C>(I, lane, r, col, base);
+        int s;
+        if (C::RV::ROWS_PER_INSTR == 1 && I < C::RV::INSTRS)
+            s = __builtin_amdgcn_readlane(sidx, I);  // one row per instruction: uniform
+        else
+            s = __shfl(sidx, r);
+        const int64_t row = s >= 0 ? s : 0;
+        __builtin_amdgcn_global_load_lds((const void*)(kvb + row * C::ROW_BYTES + col),
+                                         (lds_void*)(buf + base), 16, 0, 0);
     }
-    if (vmask != 0xffffffffu) {
-        for (int e = wv * kWave + lane; e < C::BUF / 16; e += C::THREADS) {
-            const int off = 16 * e;
-            const int r = off < RV::BYTES ? off / RV::PITCH : (off - RV::BYTES) / RR::PITCH;
-            if (!((vmask >> r) & 1u)) *(v4i*)(buf + off) = (v4i){0, 0, 0, 0};
-        }
+}
+
+// Zeroes the pieces of empty rows that this wave loaded itself (so the direct load has
+// landed before the store, in this wave's program order).  Empty rows then contribute exact
+// zeros to both products.
+template <class C>
+__device__ __forceinline__ void zero_empty_rows(uint8_t* buf, uint32_t vmask, int wv, int lane) {
+    for (int I = wv; I < C::INSTRS; I += C::NW) {
+        int r, col, base;
+        piece_of<C>(I, lane, r, col, base);
+        if (!((vmask >> r) & 1u)) *(v4i*)(buf + base + 16 * lane) = (v4i){0, 0, 0, 0};
     }
+}
+
+// Waits until at most N direct loads of this wave are still in flight (they complete in order).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int H, int DQK, int DV, bool SPLIT>
@@ -134,8 +188,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     using C = MqaCfg<H, DQK, DV>;
     using RV = typename C::RV;
     using RR = typename C::RR;
-    __shared__ __attribute__((aligned(16))) uint8_t lds0[C::BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t lds1[C::BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[3 * C::BUF];
+    __shared__ int lidx[kMaxTopk];
     __shared__ __attribute__((aligned(16))) float sx[2][2][4][kWave][4];  // [group][half][r/4][lane][r%4]
 
     // Work item.  With two workgroups per row (64 heads each) the pair is issued 8 ids
@@ -192,57 +246,66 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     const int j16 = lane & 15;
     const int vsub = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);  // value column of this tr16 lane
 
-    auto slot_index = [&](int blk) {
-        const int j = j0 + blk * kBlk + (lane & 31);
-        return j < j1 ? irow[j] : -1;
+    auto qk_off = [&](int i) {  // LDS offset of the logit operand of slice ks_begin + i
+        const int ks = min(ks_begin + i, C::KS - 1);
+        return ks < C::KSV ? RV::chunk(srow, 2 * ks + half)
+                           : RV::BYTES + RR::chunk(srow, 2 * (ks - C::KSV) + half);
     };
 
     auto compute = [&](const uint8_t* base, int sidx) {
-        const uint64_t vmask = __ballot(sidx >= 0) & 0xffffffffull;
+        const uint32_t vmask = (uint32_t)__ballot(sidx >= 0);
         // ---- partial S^T = C Q^T over this wave's dims ----
         v16f sacc = (v16f){};
-        v4i av[C::KS0];
+        {
+            v4i av[C::KS0];
 #pragma unroll
-        for (int i = 0; i < C::KS0; ++i) {  // operand loads first, so they overlap
-            const int ks = ks_begin + i;
-            const int off = ks < C::KSV ? RV::chunk(srow, 2 * ks + half)
-                                        : RV::BYTES + RR::chunk(srow, 2 * (ks - C::KSV) + half);
-            av[i] = i < nks ? *(const v4i*)(base + off) : (v4i){0, 0, 0, 0};
+            for (int i = 0; i < C::KS0; ++i) av[i] = *(const v4i*)(base + qk_off(i));
+#pragma unroll
+            for (int i = 0; i < C::KS0; ++i)
+                if (C::EVEN || i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
+            if constexpr (C::EVEN) {  // QK_AHEAD loads, then (MFMA, load) pairs, then the rest
+                __builtin_amdgcn_sched_group_barrier(0x100, C::QK_AHEAD, 0);
+#pragma unroll
+                for (int i = 0; i < C::KS0 - C::QK_AHEAD; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, C::QK_AHEAD, 0);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < C::KS0; ++i)
-            if (i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
         // ---- sum the two halves: both waves of a group form S0 + S1 in the same order ----
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
             *(v4f*)sx[hg][dp][r4][lane] =
                 (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2], sacc[4 * r4 + 3]};
         lds_barrier();
-        float s[16];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const v4f a = *(const v4f*)sx[hg][0][r4][lane];
-            const v4f b = *(const v4f*)sx[hg][1][r4][lane];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[4 * r4 + e] = a[e] + b[e];
-        }
-        if (vmask == 0ull) return;
-        // ---- online softmax: reg r <-> block row 16*(r/8) + 8*half + r%8 ----
         float z[16];
-        float mb = -INFINITY;
+        {
+            v4f a[4], b[4];
+            read_partials(lds_addr(&sx[hg][0][0][lane][0]), lds_addr(&sx[hg][1][0][lane][0]), a, b);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
-            const bool ok = (vmask >> slot) & 1ull;
-            z[r] = ok ? s[r] * sm_log2 : -INFINITY;
-            mb = fmaxf(mb, z[r]);
+            for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z[4 * r4 + e] = (a[r4][e] + b[r4][e]) * sm_log2;
         }
+        if (vmask == 0u) return;
+        // ---- online softmax: reg r <-> block row 16*(r/8) + 8*half + r%8 ----
+        if (vmask != 0xffffffffu) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
+                if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
+            }
+        }
+        float mb = z[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mb = fmaxf(mb, z[r]);
         mb = fmaxf(mb, __shfl_xor(mb, 32));
-        const bool bump = mb > m_run + 8.f;
-        const bool fresh = m_run == -INFINITY;
+        const bool bump = mb > m_run + kRescaleGap;
         if (__ballot(bump) != 0ull) {
+            const bool fresh = m_run == -INFINITY;
             const float m_new = bump ? mb : m_run;
-            const float alpha = fresh ? 0.f : exp2f(m_run - m_new);
+            const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
             if (__ballot(!fresh) != 0ull) {
@@ -258,7 +321,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pv = exp2f(z[8 * u + e] - m_run);
+                const float pv = __builtin_amdgcn_exp2f(z[8 * u + e] - m_run);
                 ls += pv;
                 pf[u][e] = (__bf16)pv;
             }
@@ -266,41 +329,52 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
         // ---- O^T += V^T P^T over this wave's value tiles ----
         // tr16 source lane j of each 16-lane group points at block row 16u + 8*half + j/4
         // (+4 for the second read), value columns vsub .. vsub+3 of the tile.
+        v8bf va[2][C::VT0];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int r_lo = 16 * u + 8 * half + (j16 >> 2);
-            v8bf va[C::VT0];
 #pragma unroll
-            for (int t = 0; t < C::VT0; ++t) {  // operand loads first, so they overlap
+            for (int t = 0; t < C::VT0; ++t) {
                 const int col = 32 * (dp * C::VT0 + t) + vsub;  // value column (bf16 index)
                 const int c = col >> 3, sub = (col & 7) * 2;
                 const v4s lo = ds_read_tr16(base + RV::chunk(r_lo, c) + sub);
                 const v4s hi = ds_read_tr16(base + RV::chunk(r_lo + 4, c) + sub);
                 const v2i l2 = __builtin_bit_cast(v2i, lo), h2 = __builtin_bit_cast(v2i, hi);
-                va[t] = __builtin_bit_cast(v8bf, (v4i){l2.x, l2.y, h2.x, h2.y});
+                va[u][t] = __builtin_bit_cast(v8bf, (v4i){l2.x, l2.y, h2.x, h2.y});
             }
-#pragma unroll
-            for (int t = 0; t < C::VT0; ++t) oacc[t] = mfma_bf16(va[t], pf[u], oacc[t]);
         }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < C::VT0; ++t) oacc[t] = mfma_bf16(va[u][t], pf[u], oacc[t]);
+        // u = 0 operands first, then its MFMAs interleaved with the u = 1 operand reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::VT0, 0);
+#pragma unroll
+        for (int t = 0; t < C::VT0; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, C::VT0, 0);
     };
 
-    // Double-buffered sweep over the blocks: loads of block b+1 fly while block b computes.
-    int s_cur = nblk > 0 ? slot_index(0) : -1;
-    if (nblk > 0) gather_block<C>(lds0, kvb, s_cur, (uint32_t)__ballot(s_cur >= 0), wv, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Index rows of the work item, staged in LDS once (-1 past its end).
+    for (int j = tid; j < nblk * kBlk; j += C::THREADS) lidx[j] = j0 + j < j1 ? irow[j0 + j] : -1;
     __syncthreads();
-    for (int blk = 0; blk < nblk; blk += 2) {
-        const int s_nxt = blk + 1 < nblk ? slot_index(blk + 1) : -1;
-        if (blk + 1 < nblk) gather_block<C>(lds1, kvb, s_nxt, (uint32_t)__ballot(s_nxt >= 0), wv, lane);
-        compute(lds0, s_cur);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (blk + 1 >= nblk) break;
-        s_cur = blk + 2 < nblk ? slot_index(blk + 2) : -1;
-        if (blk + 2 < nblk) gather_block<C>(lds0, kvb, s_cur, (uint32_t)__ballot(s_cur >= 0), wv, lane);
-        compute(lds1, s_nxt);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    auto sidx_of = [&](int blk) { return lidx[blk * kBlk + (lane & 31)]; };
+    auto buf_of = [&](int blk) { return lds + (blk % 3) * C::BUF; };
+
+    // Three-deep ring: the gathers of blocks b+1 and b+2 fly while block b computes.
+    if (nblk > 0) issue_block<C>(buf_of(0), kvb, sidx_of(0), wv, lane);
+    if (nblk > 1) issue_block<C>(buf_of(1), kvb, sidx_of(1), wv, lane);
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int s_cur = sidx_of(blk);
+        if (blk + 1 < nblk) wait_loads<C::LOADS_PER_WAVE>();  // block blk has landed ...
+        else wait_loads<0>();
+        const uint32_t vm = (uint32_t)__ballot(s_cur >= 0);
+        if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, wv, lane);
+        lds_barrier();  // ... for every wave; block blk-1's buffer is free again
+        if (blk + 2 < nblk) issue_block<C>(buf_of(blk + 2), kvb, sidx_of(blk + 2), wv, lane);
+        compute(buf_of(blk), s_cur);
     }
 
     // ---- epilogue ----
