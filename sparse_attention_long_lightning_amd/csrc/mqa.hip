@@ -93,6 +93,26 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");  // no LDS access moves above the barrier
 }
 
+// Keeps an MFMA accumulator tile in AGPRs across a join of control flow, so that the register
+// allocator does not route the loop-carried tile through VGPRs on every iteration.
+__device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); }
+
+// x *= alpha on a tile held in AGPRs, element by element through one VGPR (VALU instructions
+// cannot read AGPRs), so the tile never has to live in VGPRs.
+__device__ __forceinline__ void scale_agpr(v16f& x, float alpha) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float e = x[r], t;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n"
+            "v_mul_f32 %1, %2, %1\n"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(e), "=&v"(t)
+            : "v"(alpha));
+        x[r] = e;
+    }
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -141,24 +161,34 @@ __device__ __forceinline__ void piece_of(int I, int lane, int& r, int& col, int&
     base = rope ? RV::BYTES + Ir * 1024 : Ir * 1024;
 }
 
-// Issues the direct global->LDS loads of one block of kBlk latent rows into `buf`.  Lane l%32
-// holds the row index of block row l%32 in `sidx` (-1 = empty slot).  Every wave issues the
-// same number of instructions for every block (empty slots load row 0 of the sequence and are
-// zeroed by zero_empty_rows once they have landed), so the wait can count them.
+// Issues the direct global->LDS loads of one block of kBlk latent rows into `buf`; `rows`
+// points at the block's kBlk row indices in LDS (-1 = empty slot).  The wave's instruction
+// slots are fixed at compile time (I = wv + NW*k), so the sequence is fully unrolled: all
+// index reads first (broadcast LDS reads), then the loads.  Every wave issues the same number
+// of instructions for every block (empty slots load row 0 of the sequence and are zeroed by
+// zero_empty_rows once they have landed), so the wait can count them.
 template <class C>
-__device__ __forceinline__ void issue_block(uint8_t* buf, const uint8_t* kvb, int sidx, int wv,
-                                            int lane) {
-    for (int I = wv; I < C::INSTRS; I += C::NW) {  // same trip count on every lane
+__device__ __forceinline__ void issue_block(uint8_t* buf, const uint8_t* kvb, const int* rows,
+                                            int wv, int lane) {
+    constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
+    int s[MAXK];
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+        const int I = wv + C::NW * k;
         int r, col, base;
         piece_of<C>(I, lane, r, col, base);
-        int s;
-        if (C::RV::ROWS_PER_INSTR == 1 && I < C::RV::INSTRS)
-            s = __builtin_amdgcn_readlane(sidx, I);  // one row per instruction: uniform
-        else
-            s = __shfl(sidx, r);
-        const int64_t row = s >= 0 ? s : 0;
-        __builtin_amdgcn_global_load_lds((const void*)(kvb + row * C::ROW_BYTES + col),
-                                         (lds_void*)(buf + base), 16, 0, 0);
+        s[k] = I < C::INSTRS ? rows[r] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+        const int I = wv + C::NW * k;
+        if (I < C::INSTRS) {
+            int r, col, base;
+            piece_of<C>(I, lane, r, col, base);
+            const int64_t row = s[k] >= 0 ? s[k] : 0;
+            __builtin_amdgcn_global_load_lds((const void*)(kvb + row * C::ROW_BYTES + col),
+                                             (lds_void*)(buf + base), 16, 0, 0);
+        }
     }
 }
 
@@ -167,10 +197,15 @@ __device__ __forceinline__ void issue_block(uint8_t* buf, const uint8_t* kvb, in
 // zeros to both products.
 template <class C>
 __device__ __forceinline__ void zero_empty_rows(uint8_t* buf, uint32_t vmask, int wv, int lane) {
-    for (int I = wv; I < C::INSTRS; I += C::NW) {
-        int r, col, base;
-        piece_of<C>(I, lane, r, col, base);
-        if (!((vmask >> r) & 1u)) *(v4i*)(buf + base + 16 * lane) = (v4i){0, 0, 0, 0};
+    constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+        const int I = wv + C::NW * k;
+        if (I < C::INSTRS) {
+            int r, col, base;
+            piece_of<C>(I, lane, r, col, base);
+            if (!((vmask >> r) & 1u)) *(v4i*)(buf + base + 16 * lane) = (v4i){0, 0, 0, 0};
+        }
     }
 }
 
@@ -252,44 +287,49 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
                            : RV::BYTES + RR::chunk(srow, 2 * (ks - C::KSV) + half);
     };
 
-    auto compute = [&](const uint8_t* base, int sidx) {
-        const uint32_t vmask = (uint32_t)__ballot(sidx >= 0);
-        // ---- partial S^T = C Q^T over this wave's dims ----
+    // Partial S^T = C Q^T of one block over this wave's dims, exchanged with the other half of
+    // the head group; returns the raw logits z[16] (reg r <-> block row 16*(r/8)+8*half+r%8).
+    // Optionally evaluates `side` (the previous block's exponentials) between the MFMAs.
+    auto logits = [&](const uint8_t* base, float z[16], auto&& side) {
         v16f sacc = (v16f){};
-        {
-            v4i av[C::KS0];
+        v4i av[C::KS0];
 #pragma unroll
-            for (int i = 0; i < C::KS0; ++i) av[i] = *(const v4i*)(base + qk_off(i));
+        for (int i = 0; i < C::KS0; ++i) av[i] = *(const v4i*)(base + qk_off(i));
 #pragma unroll
-            for (int i = 0; i < C::KS0; ++i)
-                if (C::EVEN || i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
-            if constexpr (C::EVEN) {  // QK_AHEAD loads, then (MFMA, load) pairs, then the rest
-                __builtin_amdgcn_sched_group_barrier(0x100, C::QK_AHEAD, 0);
+        for (int i = 0; i < C::KS0; ++i)
+            if (C::EVEN || i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
+        side();
+        if constexpr (C::EVEN) {  // QK_AHEAD loads, then (MFMA, VALU, load) steps, then the rest
+            __builtin_amdgcn_sched_group_barrier(0x100, C::QK_AHEAD, 0);
 #pragma unroll
-                for (int i = 0; i < C::KS0 - C::QK_AHEAD; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, C::QK_AHEAD, 0);
+            for (int i = 0; i < C::KS0 - C::QK_AHEAD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < C::QK_AHEAD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
         }
-        // ---- sum the two halves: both waves of a group form S0 + S1 in the same order ----
+        // sum the two halves: both waves of a group form S0 + S1 in the same order
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
             *(v4f*)sx[hg][dp][r4][lane] =
                 (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2], sacc[4 * r4 + 3]};
         lds_barrier();
-        float z[16];
-        {
-            v4f a[4], b[4];
-            read_partials(lds_addr(&sx[hg][0][0][lane][0]), lds_addr(&sx[hg][1][0][lane][0]), a, b);
+        v4f a[4], b[4];
+        read_partials(lds_addr(&sx[hg][0][0][lane][0]), lds_addr(&sx[hg][1][0][lane][0]), a, b);
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
+        for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) z[4 * r4 + e] = (a[r4][e] + b[r4][e]) * sm_log2;
-        }
-        if (vmask == 0u) return;
-        // ---- online softmax: reg r <-> block row 16*(r/8) + 8*half + r%8 ----
+            for (int e = 0; e < 4; ++e) z[4 * r4 + e] = a[r4][e] + b[r4][e];
+    };
+
+    // Masks empty rows and updates the running max m_run (base-2 units), rescaling O when the
+    // block max exceeds it by more than kRescaleGap.  An empty block leaves everything as is.
+    auto prepare = [&](float z[16], uint32_t vmask) {
         if (vmask != 0xffffffffu) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -300,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
         float mb = z[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mb = fmaxf(mb, z[r]);
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        mb = fmaxf(mb, __shfl_xor(mb, 32)) * sm_log2;
         const bool bump = mb > m_run + kRescaleGap;
         if (__ballot(bump) != 0ull) {
             const bool fresh = m_run == -INFINITY;
@@ -310,25 +350,32 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
             l_run *= alpha;
             if (__ballot(!fresh) != 0ull) {
 #pragma unroll
-                for (int vt = 0; vt < C::VT0; ++vt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[vt][r] *= alpha;
+                for (int vt = 0; vt < C::VT0; ++vt) scale_agpr(oacc[vt], alpha);
             }
         }
-        v8bf pf[2];
+    };
+
+    // P^T of a prepared block as two bf16 B operands, p = 2^(sm_log2 * z - m_run); adds the
+    // block's row sum to l_run.  Masked rows (z = -inf) give exact zeros, also while no row has
+    // been seen (m_run = -inf is then replaced by 0).
+    auto exponentials = [&](const float z[16], v8bf pf[2]) {
+        const float mref = m_run == -INFINITY ? 0.f : m_run;
         float ls = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(z[8 * u + e] - m_run);
+                const float pv = __builtin_amdgcn_exp2f(fmaf(z[8 * u + e], sm_log2, -mref));
                 ls += pv;
                 pf[u][e] = (__bf16)pv;
             }
         l_run += ls;
-        // ---- O^T += V^T P^T over this wave's value tiles ----
-        // tr16 source lane j of each 16-lane group points at block row 16u + 8*half + j/4
-        // (+4 for the second read), value columns vsub .. vsub+3 of the tile.
+    };
+
+    // O^T += V^T P^T over this wave's value tiles.  tr16 source lane j of each 16-lane group
+    // points at block row 16u + 8*half + j/4 (+4 for the second read), value columns
+    // vsub .. vsub+3 of the tile.
+    auto values = [&](const uint8_t* base, const v8bf pf[2]) {
         v8bf va[2][C::VT0];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -360,21 +407,43 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     // Index rows of the work item, staged in LDS once (-1 past its end).
     for (int j = tid; j < nblk * kBlk; j += C::THREADS) lidx[j] = j0 + j < j1 ? irow[j0 + j] : -1;
     __syncthreads();
-    auto sidx_of = [&](int blk) { return lidx[blk * kBlk + (lane & 31)]; };
+    auto vmask_of = [&](int blk) { return (uint32_t)__ballot(lidx[blk * kBlk + (lane & 31)] >= 0); };
     auto buf_of = [&](int blk) { return lds + (blk % 3) * C::BUF; };
-
-    // Three-deep ring: the gathers of blocks b+1 and b+2 fly while block b computes.
-    if (nblk > 0) issue_block<C>(buf_of(0), kvb, sidx_of(0), wv, lane);
-    if (nblk > 1) issue_block<C>(buf_of(1), kvb, sidx_of(1), wv, lane);
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int s_cur = sidx_of(blk);
-        if (blk + 1 < nblk) wait_loads<C::LOADS_PER_WAVE>();  // block blk has landed ...
-        else wait_loads<0>();
-        const uint32_t vm = (uint32_t)__ballot(s_cur >= 0);
+    auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
+        const uint32_t vm = vmask_of(blk);
         if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, wv, lane);
+    };
+
+    // Software pipeline over the blocks (three LDS buffers): iteration b evaluates block b's
+    // exponentials under the logit MFMAs of block b+1, then block b's value product, while
+    // the gather of block b+2 flies.
+    float z[16];
+    if (nblk > 0) {
+        issue_block<C>(buf_of(0), kvb, lidx, wv, lane);
+        if (nblk > 1) issue_block<C>(buf_of(1), kvb, lidx + kBlk, wv, lane);
+        if (nblk > 1) wait_loads<C::LOADS_PER_WAVE>();
+        else wait_loads<0>();
+        land(0);
+        lds_barrier();
+        logits(buf_of(0), z, [] {});
+    }
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk + 1 < nblk) {
+            wait_loads<0>();  // block blk+1 (the only gather in flight) has landed ...
+            land(blk + 1);
+        }
         lds_barrier();  // ... for every wave; block blk-1's buffer is free again
-        if (blk + 2 < nblk) issue_block<C>(buf_of(blk + 2), kvb, sidx_of(blk + 2), wv, lane);
-        compute(buf_of(blk), s_cur);
+        if (blk + 2 < nblk) issue_block<C>(buf_of(blk + 2), kvb, lidx + (blk + 2) * kBlk, wv, lane);
+        prepare(z, vmask_of(blk));
+        v8bf pf[2];
+        float zn[16];
+        if (blk + 1 < nblk) logits(buf_of(blk + 1), zn, [&] { exponentials(z, pf); });
+        else exponentials(z, pf);
+        values(buf_of(blk), pf);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = zn[r];
+#pragma unroll
+        for (int vt = 0; vt < C::VT0; ++vt) pin_agpr(oacc[vt]);
     }
 
     // ---- epilogue ----
