@@ -161,6 +161,24 @@ __device__ __forceinline__ void piece_of(int I, int lane, int& r, int& col, int&
     base = rope ? RV::BYTES + Ir * 1024 : Ir * 1024;
 }
 
+// One direct global->LDS load of 16 bytes per lane: lane i's bytes land at lds_base + 16 * i.
+// Issued from asm so that the compiler's wait-count bookkeeping does not see it: as a FLAT
+// access that touches LDS it would otherwise turn every later LDS wait into a full drain.
+// Completion is tracked by hand with wait_loads (the load counts on vmcnt only) and a barrier
+// before any other wave reads the bytes.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber still orders it
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds_base), "v"(gaddr)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Issues the direct global->LDS loads of one block of kBlk latent rows into `buf`; `rows`
 // points at the block's kBlk row indices in LDS (-1 = empty slot).  The wave's instruction
 // slots are fixed at compile time (I = wv + NW*k), so the sequence is fully unrolled: all
@@ -171,23 +189,23 @@ template <class C>
 __device__ __forceinline__ void issue_block(uint8_t* buf, const uint8_t* kvb, const int* rows,
                                             int wv, int lane) {
     constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
+    constexpr bool FULL = C::INSTRS % C::NW == 0;  // every wave has MAXK slots
     int s[MAXK];
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
         const int I = wv + C::NW * k;
         int r, col, base;
         piece_of<C>(I, lane, r, col, base);
-        s[k] = I < C::INSTRS ? rows[r] : 0;
+        s[k] = (FULL || I < C::INSTRS) ? rows[r] : 0;
     }
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
         const int I = wv + C::NW * k;
-        if (I < C::INSTRS) {
+        if (FULL || I < C::INSTRS) {
             int r, col, base;
             piece_of<C>(I, lane, r, col, base);
-            const int64_t row = s[k] >= 0 ? s[k] : 0;
-            __builtin_amdgcn_global_load_lds((const void*)(kvb + row * C::ROW_BYTES + col),
-                                             (lds_void*)(buf + base), 16, 0, 0);
+            const uint32_t row = (uint32_t)max(s[k], 0);
+            dma16(kvb + ((uint64_t)row * C::ROW_BYTES + col), lds_addr(buf + base));
         }
     }
 }
@@ -240,7 +258,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     }
     if (row >= n_rows) return;
     const int split = SPLIT ? blockIdx.y : 0;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
     const int hg = wv & 1;  // head group: 32 heads
     const int dp = wv >> 1;  // half: logit dims and value tiles
     const RowInfo ri = row_info(map, row);
@@ -418,7 +437,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     // exponentials under the logit MFMAs of block b+1, then block b's value product, while
     // the gather of block b+2 flies.
     float z[16];
-    if (nblk > 0) {
+    if (nblk > 0) {  // the loop sits inside, so it is entered only after the prologue's waits
         issue_block<C>(buf_of(0), kvb, lidx, wv, lane);
         if (nblk > 1) issue_block<C>(buf_of(1), kvb, lidx + kBlk, wv, lane);
         if (nblk > 1) wait_loads<C::LOADS_PER_WAVE>();
@@ -426,24 +445,24 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
         land(0);
         lds_barrier();
         logits(buf_of(0), z, [] {});
-    }
-    for (int blk = 0; blk < nblk; ++blk) {
-        if (blk + 1 < nblk) {
-            wait_loads<0>();  // block blk+1 (the only gather in flight) has landed ...
-            land(blk + 1);
+        for (int blk = 0; blk < nblk; ++blk) {
+            if (blk + 1 < nblk) {
+                wait_loads<0>();  // block blk+1 (the only gather in flight) has landed ...
+                land(blk + 1);
+            }
+            lds_barrier();  // ... for every wave; block blk-1's buffer is free again
+            if (blk + 2 < nblk) issue_block<C>(buf_of(blk + 2), kvb, lidx + (blk + 2) * kBlk, wv, lane);
+            prepare(z, vmask_of(blk));
+            v8bf pf[2];
+            float zn[16];
+            if (blk + 1 < nblk) logits(buf_of(blk + 1), zn, [&] { exponentials(z, pf); });
+            else exponentials(z, pf);
+            values(buf_of(blk), pf);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = zn[r];
+#pragma unroll
+            for (int vt = 0; vt < C::VT0; ++vt) pin_agpr(oacc[vt]);
         }
-        lds_barrier();  // ... for every wave; block blk-1's buffer is free again
-        if (blk + 2 < nblk) issue_block<C>(buf_of(blk + 2), kvb, lidx + (blk + 2) * kBlk, wv, lane);
-        prepare(z, vmask_of(blk));
-        v8bf pf[2];
-        float zn[16];
-        if (blk + 1 < nblk) logits(buf_of(blk + 1), zn, [&] { exponentials(z, pf); });
-        else exponentials(z, pf);
-        values(buf_of(blk), pf);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] = zn[r];
-#pragma unroll
-        for (int vt = 0; vt < C::VT0; ++vt) pin_agpr(oacc[vt]);
     }
 
     // ---- epilogue ----
