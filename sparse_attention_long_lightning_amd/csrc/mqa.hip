@@ -23,6 +23,8 @@
 //            puts 8 consecutive block rows in each lane per 16-row k-slice).
 // LDS rows are XOR-swizzled in 16-byte chunks so that the 16 rows read together by an A
 // operand, and the 4 consecutive rows of a transpose read, fall in distinct bank groups.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -38,6 +40,8 @@ constexpr float kRescaleGap = 16.f;  // base-2 headroom before O is rescaled
 template <int NC>
 struct Region {
     static_assert(NC == 64 || NC == 8 || NC == 2, "unsupported region width");
+    static constexpr int NCH = NC;
+    static constexpr int SWZ_BITS = NC == 64 ? 4 : (NC == 8 ? 3 : 1);  // bits swz(r) can set
     static constexpr int ROWS_PER_INSTR = 64 / NC;
     static constexpr int PITCH = NC * 16;
     static constexpr int BYTES = kBlk * PITCH;
@@ -57,8 +61,11 @@ struct MqaCfg {
     static constexpr int NW = 4;
     static constexpr int NHH = (H + 63) / 64;  // workgroups per query row, 64 heads each
     static constexpr int KS = DQK / 16;        // k-slices of the logit product
-    static constexpr int KS0 = (KS + 1) / 2;   // slices of half 0 (half 1 takes the rest)
     static constexpr int KSV = DV / 16;        // k-slices that fall in the value region
+    static constexpr int KSV2 = KSV / 2;       // value slices per half
+    static constexpr int R = KS - KSV;         // rope slices
+    static constexpr int RH = (R + 1) / 2;     // rope slices of half 0 (half 1 takes the rest)
+    static constexpr int KS0 = KSV2 + RH;      // slices of half 0 (the larger half)
     static constexpr int VT = DV / 32;         // 32-wide value tiles
     static constexpr int VT0 = VT / 2;         // value tiles per half
     using RV = Region<DV * 2 / 16>;
@@ -68,8 +75,13 @@ struct MqaCfg {
     static constexpr int ROW_BYTES = DQK * 2;           // bytes of one latent row in memory
     static constexpr int VBYTES = DV * 2;               // bytes of its value part
     static constexpr int LOADS_PER_WAVE = INSTRS / NW;  // direct loads per wave and block (min)
-    static constexpr bool EVEN = KS % 2 == 0;           // both halves have KS0 slices
+    static constexpr bool EVEN = R % 2 == 0;            // both halves have KS0 slices
     static constexpr int QK_AHEAD = KS0 < 9 ? KS0 : 9;  // logit operand loads kept in flight
+    // Per-lane LDS offsets are kept for TLQ logit slices and TLV value tiles only: the rest
+    // differ by a multiple of the swizzle period and reach the reads as immediate offsets.
+    static constexpr int W = RV::SWZ_BITS;
+    static constexpr int TLQ = (KSV % (1 << W) == 0 && KSV2 % (1 << (W - 1)) == 0) ? (1 << (W - 1)) : KSV2;
+    static constexpr int TLV = ((4 * VT0) % (1 << W) == 0 && VT0 % (1 << (W - 2)) == 0) ? (1 << (W - 2)) : VT0;
     static_assert(DQK % 16 == 0 && DV % 64 == 0, "unsupported latent widths");
     static_assert(NHH <= 2, "at most 128 heads");
 };
@@ -81,9 +93,15 @@ __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ v4s ds_read_tr16(const uint8_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+
+// LDS accesses by 32-bit LDS byte address (a uniform buffer base plus a per-lane offset, so a
+// read costs one add and constant parts ride in the instruction's offset field).
+__device__ __forceinline__ v4s ds_read_tr16(uint32_t a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(size_t)a);
 }
+__device__ __forceinline__ v4i lds_read16(uint32_t a) { return *(const lds_v4i*)(size_t)a; }
+__device__ __forceinline__ void lds_write16(uint32_t a, v4i v) { *(lds_v4i*)(size_t)a = v; }
 
 // Workgroup barrier that orders LDS accesses only: in-flight direct global->LDS loads into
 // the other buffers are not waited for (the fence of a full __syncthreads would drain them).
@@ -96,6 +114,9 @@ __device__ __forceinline__ void lds_barrier() {
 // Keeps an MFMA accumulator tile in AGPRs across a join of control flow, so that the register
 // allocator does not route the loop-carried tile through VGPRs on every iteration.
 __device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); }
+
+// Keeps a query fragment (an MFMA B operand, read as is from AGPRs) out of the VGPRs.
+__device__ __forceinline__ void pin_agpr(v8bf& x) { asm volatile("" : "+a"(x)); }
 
 // x *= alpha on a tile held in AGPRs, element by element through one VGPR (VALU instructions
 // cannot read AGPRs), so the tile never has to live in VGPRs.
@@ -161,42 +182,42 @@ __device__ __forceinline__ void piece_of(int I, int lane, int& r, int& col, int&
     base = rope ? RV::BYTES + Ir * 1024 : Ir * 1024;
 }
 
-// One direct global->LDS load of 16 bytes per lane: lane i's bytes land at lds_base + 16 * i.
-// Issued from asm so that the compiler's wait-count bookkeeping does not see it: as a FLAT
-// access that touches LDS it would otherwise turn every later LDS wait into a full drain.
-// Completion is tracked by hand with wait_loads (the load counts on vmcnt only) and a barrier
-// before any other wave reads the bytes.
+// One direct global->LDS load of 16 bytes per lane from kvb + off: lane i's bytes land at
+// lds_base + 16 * i.  Issued from asm so that the compiler's wait-count bookkeeping does not
+// see it: as a FLAT access that touches LDS it would otherwise turn every later LDS wait into
+// a full drain.  Completion is tracked by hand with wait_loads (the load counts on vmcnt only)
+// and a barrier before any other wave reads the bytes.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber still orders it
-__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+__device__ __forceinline__ void dma16(const uint8_t* kvb, uint32_t off, uint32_t lds_base) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off"
+        "global_load_lds_dwordx4 %1, %2"
         :
-        : "s"(lds_base), "v"(gaddr)
+        : "s"(lds_base), "v"(off), "s"(kvb)
         : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
-// Issues the direct global->LDS loads of one block of kBlk latent rows into `buf`; `rows`
-// points at the block's kBlk row indices in LDS (-1 = empty slot).  The wave's instruction
-// slots are fixed at compile time (I = wv + NW*k), so the sequence is fully unrolled: all
-// index reads first (broadcast LDS reads), then the loads.  Every wave issues the same number
-// of instructions for every block (empty slots load row 0 of the sequence and are zeroed by
-// zero_empty_rows once they have landed), so the wait can count them.
+// Issues the direct global->LDS loads of one block of kBlk latent rows into the buffer at
+// LDS address `buf`; `offs` points at the block's kBlk row byte offsets in LDS (empty slots
+// hold 0, i.e. row 0 of the sequence, and are zeroed by zero_empty_rows once landed).  The
+// wave's instruction slots are fixed at compile time (I = wv + NW*k), so the sequence is
+// fully unrolled: all offset reads first, then the loads.  Every wave issues the same number
+// of instructions for every block, so the wait can count them.
 template <class C>
-__device__ __forceinline__ void issue_block(uint8_t* buf, const uint8_t* kvb, const int* rows,
+__device__ __forceinline__ void issue_block(uint32_t buf, const uint8_t* kvb, const uint32_t* offs,
                                             int wv, int lane) {
     constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
     constexpr bool FULL = C::INSTRS % C::NW == 0;  // every wave has MAXK slots
-    int s[MAXK];
+    uint32_t o[MAXK];
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
         const int I = wv + C::NW * k;
         int r, col, base;
         piece_of<C>(I, lane, r, col, base);
-        s[k] = (FULL || I < C::INSTRS) ? rows[r] : 0;
+        o[k] = (FULL || I < C::INSTRS) ? offs[r] + col : 0u;
     }
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
@@ -204,8 +225,7 @@ __device__ __forceinline__ void issue_block(uint8_t* buf, const uint8_t* kvb, co
         if (FULL || I < C::INSTRS) {
             int r, col, base;
             piece_of<C>(I, lane, r, col, base);
-            const uint32_t row = (uint32_t)max(s[k], 0);
-            dma16(kvb + ((uint64_t)row * C::ROW_BYTES + col), lds_addr(buf + base));
+            dma16(kvb, o[k], buf + base);
         }
     }
 }
@@ -214,7 +234,7 @@ __device__ __forceinline__ void issue_block(uint8_t* buf, const uint8_t* kvb, co
 // landed before the store, in this wave's program order).  Empty rows then contribute exact
 // zeros to both products.
 template <class C>
-__device__ __forceinline__ void zero_empty_rows(uint8_t* buf, uint32_t vmask, int wv, int lane) {
+__device__ __forceinline__ void zero_empty_rows(uint32_t buf, uint32_t vmask, int wv, int lane) {
     constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
@@ -222,7 +242,7 @@ __device__ __forceinline__ void zero_empty_rows(uint8_t* buf, uint32_t vmask, in
         if (I < C::INSTRS) {
             int r, col, base;
             piece_of<C>(I, lane, r, col, base);
-            if (!((vmask >> r) & 1u)) *(v4i*)(buf + base + 16 * lane) = (v4i){0, 0, 0, 0};
+            if (!((vmask >> r) & 1u)) lds_write16(buf + base + 16 * lane, (v4i){0, 0, 0, 0});
         }
     }
 }
@@ -242,7 +262,8 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     using RV = typename C::RV;
     using RR = typename C::RR;
     __shared__ __attribute__((aligned(16))) uint8_t lds[3 * C::BUF];
-    __shared__ int lidx[kMaxTopk];
+    __shared__ uint32_t lofs[kMaxTopk];            // byte offset of each selected row (0 if empty)
+    __shared__ uint32_t lmask[kMaxTopk / kBlk];    // per block: bit j = slot j holds a row
     __shared__ __attribute__((aligned(16))) float sx[2][2][4][kWave][4];  // [group][half][r/4][lane][r%4]
 
     // Work item.  With two workgroups per row (64 heads each) the pair is issued 8 ids
@@ -270,20 +291,23 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     const int32_t* irow = idx + (int64_t)row * topk;
     const uint8_t* kvb = (const uint8_t*)(kv + (int64_t)ri.kbase * DQK);
 
-    // Query fragments of this wave's half of the dims: lane l holds head 64*hh + 32*hg + l%32,
-    // dims 16*ks + 8*(l/32) .. +7 for ks in [ks_begin, ks_begin + nks).
+    // Logit k-slices of this wave's half: value slices dp*KSV2 + i (i < KSV2), then rope
+    // slices KSV + dp*RH + j.  Lane l holds head 64*hh + 32*hg + l%32, dims 8*(l/32) .. +7 of
+    // each slice.
     const int head = hh * 64 + hg * 32 + (lane & 31);
     const int half = lane >> 5;
-    const int ks_begin = dp ? C::KS0 : 0;
-    const int nks = dp ? C::KS - C::KS0 : C::KS0;
+    const int nrope = min(C::RH, C::R - dp * C::RH);  // rope slices of this half
+    const int nks = C::KSV2 + nrope;
     v8bf qf[C::KS0];
     {
         const uint16_t* qp = q + ((int64_t)ri.qrow * H + (head < H ? head : 0)) * DQK + 8 * half;
 #pragma unroll
         for (int i = 0; i < C::KS0; ++i) {
+            const int ks = i < C::KSV2 ? dp * C::KSV2 + i : C::KSV + dp * C::RH + (i - C::KSV2);
             v4i v = {0, 0, 0, 0};
-            if (head < H && i < nks) v = *(const v4i*)(qp + 16 * (ks_begin + i));
+            if (head < H && i < nks) v = *(const v4i*)(qp + 16 * ks);
             qf[i] = __builtin_bit_cast(v8bf, v);
+            pin_agpr(qf[i]);
         }
     }
 
@@ -298,57 +322,80 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     const int mi = lane & 31;
     const int srow = 16 * (mi >> 4) + 8 * ((mi >> 2) & 1) + 4 * ((mi >> 3) & 1) + (mi & 3);
     const int j16 = lane & 15;
-    const int vsub = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);  // value column of this tr16 lane
 
-    auto qk_off = [&](int i) {  // LDS offset of the logit operand of slice ks_begin + i
-        const int ks = min(ks_begin + i, C::KS - 1);
-        return ks < C::KSV ? RV::chunk(srow, 2 * ks + half)
-                           : RV::BYTES + RR::chunk(srow, 2 * (ks - C::KSV) + half);
+    // Per-lane LDS offsets within a block buffer.
+    //  logit operand of value slice i: qoff[i % TLQ] + 32*TLQ*(i / TLQ);
+    //  logit operand of rope slice j:  roff[j];
+    //  value operand (tr16 read) of 16-row slice u, row quad h, tile t:
+    //      voff[u][h][t % TLV] + 64*TLV*(t / TLV).
+    // tr16 source lane j of each 16-lane group points at block row 16u + 8*half + j/4 (+4 for
+    // h = 1) and value columns cl*8 + sub/2 .. +3 of the tile.
+    uint32_t qoff[C::TLQ], roff[C::RH], voff[2][2][C::TLV];
+#pragma unroll
+    for (int i = 0; i < C::TLQ; ++i) qoff[i] = RV::chunk(srow, dp * C::KSV + 2 * i + half);
+#pragma unroll
+    for (int j = 0; j < C::RH; ++j) roff[j] = RV::BYTES + RR::chunk(srow, 2 * (dp * C::RH + j) + half);
+    {
+        const int vsub = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);  // value column of this tr16 lane
+        const int cl = vsub >> 3, sub = (vsub & 7) * 2;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int t = 0; t < C::TLV; ++t)
+                    voff[u][h][t] = RV::chunk(16 * u + 8 * half + (j16 >> 2) + 4 * h,
+                                              4 * (dp * C::VT0 + t) + cl) + sub;
+    }
+    const uint32_t lds0 = lds_addr(lds);
+    const uint32_t sx_own = lds_addr(&sx[hg][dp][0][lane][0]);
+    const uint32_t sx0 = lds_addr(&sx[hg][0][0][lane][0]);
+    const uint32_t sx1 = lds_addr(&sx[hg][1][0][lane][0]);
+
+    // Selected rows of the work item, staged in LDS once: byte offsets (row 0 for an empty
+    // slot) and per-block occupancy masks.  A row's offset must fit in 31 bits.
+    for (int j = tid; j < nblk * kBlk; j += C::THREADS) {
+        const int id = j0 + j < j1 ? irow[j0 + j] : -1;
+        lofs[j] = id >= 0 ? (uint32_t)id * (uint32_t)C::ROW_BYTES : 0u;
+        const uint64_t m = __ballot(id >= 0);
+        if (lane == 0) lmask[j >> 5] = (uint32_t)m;
+        if (lane == 32) lmask[j >> 5] = (uint32_t)(m >> 32);
+    }
+    __syncthreads();
+
+    // LDS address of block blk's buffer.  Passed through readfirstlane so that it stays one
+    // opaque scalar per step: otherwise the compiler strength-reduces it into per-lane
+    // induction variables and loses the immediate offsets of the reads.
+    auto buf_of = [&](int blk) {
+        return (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(blk % 3) * C::BUF);
+    };
+    auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
+        const uint32_t vm = lmask[blk];
+        if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, wv, lane);
+    };
+    // Per-lane addresses base + off, made opaque so that constant parts added afterwards go
+    // into the instructions' offset field instead of into one add per read.
+    auto opaque = [](uint32_t x) {
+        asm volatile("" : "+v"(x));
+        return x;
     };
 
-    // Partial S^T = C Q^T of one block over this wave's dims, exchanged with the other half of
-    // the head group; returns the raw logits z[16] (reg r <-> block row 16*(r/8)+8*half+r%8).
-    // Optionally evaluates `side` (the previous block's exponentials) between the MFMAs.
-    auto logits = [&](const uint8_t* base, float z[16], auto&& side) {
-        v16f sacc = (v16f){};
-        v4i av[C::KS0];
-#pragma unroll
-        for (int i = 0; i < C::KS0; ++i) av[i] = *(const v4i*)(base + qk_off(i));
-#pragma unroll
-        for (int i = 0; i < C::KS0; ++i)
-            if (C::EVEN || i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
-        side();
-        if constexpr (C::EVEN) {  // QK_AHEAD loads, then (MFMA, VALU, load) steps, then the rest
-            __builtin_amdgcn_sched_group_barrier(0x100, C::QK_AHEAD, 0);
-#pragma unroll
-            for (int i = 0; i < C::KS0 - C::QK_AHEAD; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < C::QK_AHEAD; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            }
-        }
-        // sum the two halves: both waves of a group form S0 + S1 in the same order
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            *(v4f*)sx[hg][dp][r4][lane] =
-                (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2], sacc[4 * r4 + 3]};
-        lds_barrier();
-        v4f a[4], b[4];
-        read_partials(lds_addr(&sx[hg][0][0][lane][0]), lds_addr(&sx[hg][1][0][lane][0]), a, b);
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[4 * r4 + e] = a[r4][e] + b[r4][e];
+    // ---- phase pieces ----
+    // Logit operand of slice i of this wave's half (value slices, then rope slices).
+    auto qk_read = [&](const uint32_t (&qa)[C::TLQ], const uint32_t (&ra)[C::RH], int i) {
+        if (i < C::KSV2) return lds_read16(qa[i % C::TLQ] + 32 * C::TLQ * (i / C::TLQ));
+        return lds_read16(ra[i - C::KSV2]);
     };
-
-    // Masks empty rows and updates the running max m_run (base-2 units), rescaling O when the
-    // block max exceeds it by more than kRescaleGap.  An empty block leaves everything as is.
-    auto prepare = [&](float z[16], uint32_t vmask) {
+    // p = 2^(sm_log2 * z - m_run) of element e; masked rows (z = -inf) give exact zeros,
+    // also while no row has been seen (m_run = -inf is then replaced by 0).
+    auto exp_elem = [&](const float (&zc)[16], int e, float mref, float (&pe)[16], float& ls) {
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(zc[e], sm_log2, -mref));
+        ls += pe[e];
+    };
+    // Masks empty rows of a block's logits and folds them into the running max m_run (base-2
+    // units); returns the rescale factor for O and l (1 when the max did not jump by more
+    // than kRescaleGap, 0 for the first rows seen).
+    auto block_max = [&](float (&z)[16], uint32_t vmask) {
         if (vmask != 0xffffffffu) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -356,10 +403,13 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
                 if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
             }
         }
-        float mb = z[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mb = fmaxf(mb, z[r]);
+        float mb = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+        mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(z[8], z[9]), fmaxf(z[10], z[11])),
+                             fmaxf(fmaxf(z[12], z[13]), fmaxf(z[14], z[15]))));
         mb = fmaxf(mb, __shfl_xor(mb, 32)) * sm_log2;
+        return mb;
+    };
+    auto rescale = [&](float mb) {
         const bool bump = mb > m_run + kRescaleGap;
         if (__ballot(bump) != 0ull) {
             const bool fresh = m_run == -INFINITY;
@@ -368,100 +418,216 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
             m_run = m_new;
             l_run *= alpha;
             if (__ballot(!fresh) != 0ull) {
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // MFMA results settle
 #pragma unroll
                 for (int vt = 0; vt < C::VT0; ++vt) scale_agpr(oacc[vt], alpha);
+                asm volatile("s_nop 4" ::: "memory");  // before the next MFMA reads them
             }
         }
     };
 
-    // P^T of a prepared block as two bf16 B operands, p = 2^(sm_log2 * z - m_run); adds the
-    // block's row sum to l_run.  Masked rows (z = -inf) give exact zeros, also while no row has
-    // been seen (m_run = -inf is then replaced by 0).
-    auto exponentials = [&](const float z[16], v8bf pf[2]) {
-        const float mref = m_run == -INFINITY ? 0.f : m_run;
-        float ls = 0.f;
+    // Phase B of a step: S^T partial of block `nb` (next) with the logit MFMAs (when QK),
+    // while block `zc`'s exponentials (when EXP) and the direct loads of block `db` (when DMA)
+    // fill the gaps between them.  Program order is fixed with scheduling barriers; the
+    // compiler then waits for each operand read only as far as needed.
+    constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
+    constexpr int AHEAD = C::KS0 < 6 ? C::KS0 : 6;
+    auto phase_b = [&](uint32_t nb, const float (&zc)[16], v8bf (&pf)[2], int db, auto QK, auto EXP,
+                       auto DMA) -> v16f {
+        constexpr bool do_qk = decltype(QK)::value, do_exp = decltype(EXP)::value;
+        constexpr bool do_dma = decltype(DMA)::value;
+        uint32_t o[MAXK];
+        uint32_t dbuf = 0;
+        if constexpr (do_dma) {
+            dbuf = buf_of(db);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(z[8 * u + e], sm_log2, -mref));
-                ls += pv;
-                pf[u][e] = (__bf16)pv;
+            for (int k = 0; k < MAXK; ++k) {
+                const int I = wv + C::NW * k;
+                int r, col, base;
+                piece_of<C>(I, lane, r, col, base);
+                o[k] = (C::INSTRS % C::NW == 0 || I < C::INSTRS) ? lofs[db * kBlk + r] + col : 0u;
             }
-        l_run += ls;
+        }
+        auto dma_k = [&](int k) {
+            const int I = wv + C::NW * k;
+            if (C::INSTRS % C::NW == 0 || I < C::INSTRS) {
+                int r, col, base;
+                piece_of<C>(I, lane, r, col, base);
+                dma16(kvb, o[k], dbuf + base);
+            }
+        };
+        uint32_t qa[C::TLQ], ra[C::RH];
+        v4i av[C::KS0];
+        if constexpr (do_qk) {
+#pragma unroll
+            for (int i = 0; i < C::TLQ; ++i) qa[i] = opaque(nb + qoff[i]);
+#pragma unroll
+            for (int j = 0; j < C::RH; ++j) ra[j] = opaque(nb + roff[j]);
+#pragma unroll
+            for (int i = 0; i < AHEAD; ++i) av[i] = qk_read(qa, ra, i);
+        }
+        const float mref = m_run == -INFINITY ? 0.f : m_run;
+        float pe[16], ls = 0.f;
+        v16f sacc = (v16f){};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < C::KS0; ++i) {
+            if constexpr (do_qk) {
+                if (i + AHEAD < C::KS0) av[i + AHEAD] = qk_read(qa, ra, i + AHEAD);
+                if (C::EVEN || i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
+            }
+            if constexpr (do_exp)
+                if (i < 16) exp_elem(zc, i, mref, pe, ls);
+            if constexpr (do_dma)
+                if (i < MAXK) dma_k(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (do_exp) {
+#pragma unroll
+            for (int e = C::KS0; e < 16; ++e) exp_elem(zc, e, mref, pe, ls);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pf[u][e] = (__bf16)pe[8 * u + e];
+            l_run += ls;
+        }
+        if constexpr (do_dma) {
+#pragma unroll
+            for (int k = C::KS0; k < MAXK; ++k) dma_k(k);
+        }
+        return sacc;
     };
 
-    // O^T += V^T P^T over this wave's value tiles.  tr16 source lane j of each 16-lane group
-    // points at block row 16u + 8*half + j/4 (+4 for the second read), value columns
-    // vsub .. vsub+3 of the tile.
-    auto values = [&](const uint8_t* base, const v8bf pf[2]) {
-        v8bf va[2][C::VT0];
+    // Phase C: both halves of a head group publish their partial S^T.
+    auto phase_c = [&](const v16f& sacc) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int r_lo = 16 * u + 8 * half + (j16 >> 2);
+        for (int r4 = 0; r4 < 4; ++r4)
+            lds_write16(sx_own + 1024 * r4,
+                        __builtin_bit_cast(v4i, (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2],
+                                                      sacc[4 * r4 + 3]}));
+        lds_barrier();
+    };
+
+    // Phase D: O^T += V^T P^T for block `cb` (when PV), while the summed logits zn of the
+    // next block are read and reduced to their max (when NEXT).
+    auto phase_d = [&](uint32_t cb, const v8bf (&pf)[2], float (&zn)[16], uint32_t vmask_n, auto PV,
+                       auto NEXT) {
+        constexpr bool do_pv = decltype(PV)::value, do_next = decltype(NEXT)::value;
+        uint32_t va_[2][2][C::TLV];
+        v8bf va[2][C::VT0];
+        auto vread = [&](int u, int t) {
+            const uint32_t imm = 64 * C::TLV * (t / C::TLV);
+            const v4s lo = ds_read_tr16(va_[u][0][t % C::TLV] + imm);
+            const v4s hi = ds_read_tr16(va_[u][1][t % C::TLV] + imm);
+            const v2i l2 = __builtin_bit_cast(v2i, lo), h2 = __builtin_bit_cast(v2i, hi);
+            return __builtin_bit_cast(v8bf, (v4i){l2.x, l2.y, h2.x, h2.y});
+        };
+        if constexpr (do_pv) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int t = 0; t < C::TLV; ++t) va_[u][h][t] = opaque(cb + voff[u][h][t]);
+#pragma unroll
+            for (int t = 0; t < C::VT0; ++t) va[0][t] = vread(0, t);
+        }
+        v4f a[4], b[4];
+        if constexpr (do_next) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                a[r4] = __builtin_bit_cast(v4f, lds_read16(sx0 + 1024 * r4));
+                b[r4] = __builtin_bit_cast(v4f, lds_read16(sx1 + 1024 * r4));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (do_pv) {
 #pragma unroll
             for (int t = 0; t < C::VT0; ++t) {
-                const int col = 32 * (dp * C::VT0 + t) + vsub;  // value column (bf16 index)
-                const int c = col >> 3, sub = (col & 7) * 2;
-                const v4s lo = ds_read_tr16(base + RV::chunk(r_lo, c) + sub);
-                const v4s hi = ds_read_tr16(base + RV::chunk(r_lo + 4, c) + sub);
-                const v2i l2 = __builtin_bit_cast(v2i, lo), h2 = __builtin_bit_cast(v2i, hi);
-                va[u][t] = __builtin_bit_cast(v8bf, (v4i){l2.x, l2.y, h2.x, h2.y});
+                va[1][t] = vread(1, t);
+                oacc[t] = mfma_bf16(va[0][t], pf[0], oacc[t]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int t = 0; t < C::VT0; ++t) oacc[t] = mfma_bf16(va[u][t], pf[u], oacc[t]);
-        // u = 0 operands first, then its MFMAs interleaved with the u = 1 operand reads
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::VT0, 0);
-#pragma unroll
         for (int t = 0; t < C::VT0; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if constexpr (do_pv) oacc[t] = mfma_bf16(va[1][t], pf[1], oacc[t]);
+            if constexpr (do_next) {
+#pragma unroll
+                for (int k = 0; k < 16 / C::VT0; ++k) {
+                    const int r = t * (16 / C::VT0) + k;
+                    zn[r] = a[r >> 2][r & 3] + b[r >> 2][r & 3];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, C::VT0, 0);
+        if constexpr (do_next) {
+#pragma unroll
+            for (int r = C::VT0 * (16 / C::VT0); r < 16; ++r) zn[r] = a[r >> 2][r & 3] + b[r >> 2][r & 3];
+            rescale(block_max(zn, vmask_n));
+        }
+#pragma unroll
+        for (int vt = 0; vt < C::VT0; ++vt) pin_agpr(oacc[vt]);
     };
 
-    // Index rows of the work item, staged in LDS once (-1 past its end).
-    for (int j = tid; j < nblk * kBlk; j += C::THREADS) lidx[j] = j0 + j < j1 ? irow[j0 + j] : -1;
-    __syncthreads();
-    auto vmask_of = [&](int blk) { return (uint32_t)__ballot(lidx[blk * kBlk + (lane & 31)] >= 0); };
-    auto buf_of = [&](int blk) { return lds + (blk % 3) * C::BUF; };
-    auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
-        const uint32_t vm = vmask_of(blk);
-        if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, wv, lane);
+    // Software pipeline over the blocks (three LDS buffers).  Step b, with the logits of block
+    // b in zc and its max folded into m_run:
+    //   top  block b+1's loads have landed (own wait, then a barrier); block b-1's buffer is free
+    //   B    logit MFMAs of block b+1, with block b's exponentials and block b+2's direct loads
+    //   C    exchange of block b+1's partial logits
+    //   D    value MFMAs of block b, with block b+1's logits summed and reduced to their max.
+    // The steady state (b+2 < nblk) runs unrolled by two, the logits alternating between za and
+    // zb; the last steps take the general form.
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    auto top = [&](int blk) {
+        if (blk + 1 < nblk) {
+            wait_loads<0>();
+            land(blk + 1);
+        }
+        lds_barrier();
     };
-
-    // Software pipeline over the blocks (three LDS buffers): iteration b evaluates block b's
-    // exponentials under the logit MFMAs of block b+1, then block b's value product, while
-    // the gather of block b+2 flies.
-    float z[16];
+    auto step_full = [&](int blk, float (&zc)[16], float (&zn)[16]) {
+        top(blk);
+        v8bf pf[2];
+        phase_c(phase_b(buf_of(blk + 1), zc, pf, blk + 2, T_{}, T_{}, T_{}));
+        phase_d(buf_of(blk), pf, zn, lmask[blk + 1], T_{}, T_{});
+    };
+    auto step_tail = [&](int blk, float (&zc)[16], float (&zn)[16]) {
+        top(blk);
+        v8bf pf[2];
+        if (blk + 2 < nblk) {
+            phase_c(phase_b(buf_of(blk + 1), zc, pf, blk + 2, T_{}, T_{}, T_{}));
+            phase_d(buf_of(blk), pf, zn, lmask[blk + 1], T_{}, T_{});
+        } else if (blk + 1 < nblk) {
+            phase_c(phase_b(buf_of(blk + 1), zc, pf, 0, T_{}, T_{}, F_{}));
+            phase_d(buf_of(blk), pf, zn, lmask[blk + 1], T_{}, T_{});
+        } else {
+            phase_b(0u, zc, pf, 0, F_{}, T_{}, F_{});
+            phase_d(buf_of(blk), pf, zn, 0u, T_{}, F_{});
+        }
+    };
     if (nblk > 0) {  // the loop sits inside, so it is entered only after the prologue's waits
-        issue_block<C>(buf_of(0), kvb, lidx, wv, lane);
-        if (nblk > 1) issue_block<C>(buf_of(1), kvb, lidx + kBlk, wv, lane);
+        float za[16], zb[16];
+        v8bf pf0[2];
+        issue_block<C>(buf_of(0), kvb, lofs, wv, lane);
+        if (nblk > 1) issue_block<C>(buf_of(1), kvb, lofs + kBlk, wv, lane);
         if (nblk > 1) wait_loads<C::LOADS_PER_WAVE>();
         else wait_loads<0>();
         land(0);
         lds_barrier();
-        logits(buf_of(0), z, [] {});
-        for (int blk = 0; blk < nblk; ++blk) {
-            if (blk + 1 < nblk) {
-                wait_loads<0>();  // block blk+1 (the only gather in flight) has landed ...
-                land(blk + 1);
-            }
-            lds_barrier();  // ... for every wave; block blk-1's buffer is free again
-            if (blk + 2 < nblk) issue_block<C>(buf_of(blk + 2), kvb, lidx + (blk + 2) * kBlk, wv, lane);
-            prepare(z, vmask_of(blk));
-            v8bf pf[2];
-            float zn[16];
-            if (blk + 1 < nblk) logits(buf_of(blk + 1), zn, [&] { exponentials(z, pf); });
-            else exponentials(z, pf);
-            values(buf_of(blk), pf);
+        phase_c(phase_b(buf_of(0), za, pf0, 0, T_{}, F_{}, F_{}));
+        phase_d(0u, pf0, za, lmask[0], F_{}, T_{});
+        int blk = 0;
+        for (; blk + 3 < nblk; blk += 2) {
+            step_full(blk, za, zb);
+            step_full(blk + 1, zb, za);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = zn[r];
-#pragma unroll
-            for (int vt = 0; vt < C::VT0; ++vt) pin_agpr(oacc[vt]);
+            for (int i = 0; i < C::KS0; ++i) pin_agpr(qf[i]);
+        }
+        while (blk < nblk) {
+            step_tail(blk++, za, zb);
+            if (blk < nblk) step_tail(blk++, zb, za);
         }
     }
 
