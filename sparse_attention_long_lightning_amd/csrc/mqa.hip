@@ -388,9 +388,12 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     };
     // p = 2^(sm_log2 * z - m_run) of element e; masked rows (z = -inf) give exact zeros,
     // also while no row has been seen (m_run = -inf is then replaced by 0).
+    // The empty asm anchors each result at its place in the fixed program order (plain
+    // arithmetic would otherwise be sunk past the scheduling barriers to its first use).
     auto exp_elem = [&](const float (&zc)[16], int e, float mref, float (&pe)[16], float& ls) {
         pe[e] = __builtin_amdgcn_exp2f(fmaf(zc[e], sm_log2, -mref));
         ls += pe[e];
+        asm volatile("" : "+v"(pe[e]), "+v"(ls));
     };
     // Masks empty rows of a block's logits and folds them into the running max m_run (base-2
     // units); returns the rescale factor for O and l (1 when the max did not jump by more
@@ -403,10 +406,12 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
                 if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
             }
         }
-        float mb = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-        mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(z[8], z[9]), fmaxf(z[10], z[11])),
-                             fmaxf(fmaxf(z[12], z[13]), fmaxf(z[14], z[15]))));
-        mb = fmaxf(mb, __shfl_xor(mb, 32)) * sm_log2;
+        // med3(a, b, +inf) = max(a, b) for the non-NaN logits here; unlike fmaxf it needs no
+        // quieting of its inputs first
+        float mb = __builtin_amdgcn_fmed3f(z[0], z[1], INFINITY);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mb = __builtin_amdgcn_fmed3f(mb, z[r], INFINITY);
+        mb = __builtin_amdgcn_fmed3f(mb, __shfl_xor(mb, 32), INFINITY) * sm_log2;
         return mb;
     };
     auto rescale = [&](float mb) {
@@ -557,6 +562,7 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
                 for (int k = 0; k < 16 / C::VT0; ++k) {
                     const int r = t * (16 / C::VT0) + k;
                     zn[r] = a[r >> 2][r & 3] + b[r >> 2][r & 3];
+                    asm volatile("" : "+v"(zn[r]));
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
