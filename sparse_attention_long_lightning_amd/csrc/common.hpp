@@ -90,4 +90,70 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
+
+// ---- LDS and direct global->LDS helpers ----
+
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+
+// LDS accesses by 32-bit LDS byte address (a uniform buffer base plus a per-lane offset, so a
+// read costs one add and constant parts ride in the instruction's offset field).
+__device__ __forceinline__ v4s ds_read_tr16(uint32_t a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(size_t)a);
+}
+__device__ __forceinline__ v4i lds_read16(uint32_t a) { return *(const lds_v4i*)(size_t)a; }
+__device__ __forceinline__ void lds_write16(uint32_t a, v4i v) { *(lds_v4i*)(size_t)a = v; }
+
+// Workgroup barrier that orders LDS accesses only: in-flight direct global->LDS loads into
+// the other buffers are not waited for (the fence of a full __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS access moves above the barrier
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+
+// One direct global->LDS load of 16 bytes per lane from base + off: lane i's bytes land at
+// lds_base + 16 * i.  Issued from asm so that the compiler's wait-count bookkeeping does not
+// see it: as a FLAT access that touches LDS it would otherwise turn every later LDS wait into
+// a full drain.  Completion is tracked by hand with wait_loads (the load counts on vmcnt only)
+// and a barrier before any other wave reads the bytes.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber still orders it
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_base), "v"(off), "s"(base)
+        : "memory", "m0");
+}
+// The same with 4 bytes per lane: lane i's dword lands at lds_base + 4 * i.
+__device__ __forceinline__ void dma4(const void* base, uint32_t off, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2"
+        :
+        : "s"(lds_base), "v"(off), "s"(base)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Waits until at most N vector memory operations of this wave are still in flight.  Loads
+// complete in issue order, so waiting down to the number of loads issued after a given one
+// guarantees that one has landed; stores also count here but may finish out of order, so a
+// caller counts only younger loads (younger stores can only make the wait longer).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace dsa

@@ -31,50 +31,61 @@ __device__ __forceinline__ float sum_over_groups(float v) {
     return v;
 }
 
-constexpr int kPrefillTokens = 8;    // query tokens per workgroup (2 per wave)
-constexpr int kPrefillKeys = 512;    // keys per workgroup tile
-constexpr int kPrefillThreads = 256;
+constexpr int kIxTokens = 16;    // query tokens per workgroup (2 per wave)
+constexpr int kIxThreads = 512;  // 8 waves: two per SIMD, so one wave's epilogue runs under
+                                 // the other's MFMAs
+constexpr int kIxWaves = kIxThreads / kWave;
+constexpr int kIxTile = 256;     // keys per LDS tile
+constexpr int kIxSeg = 4096;     // keys per workgroup: a run of tiles through a 3-deep ring
+constexpr int kIxBufs = 3;
 
-// One workgroup scores kPrefillTokens consecutive query rows of one sequence against one
-// span of kPrefillKeys keys.  The key span is staged in LDS once; each wave keeps the FP8
-// query fragments of its two tokens in registers and sweeps the span 16 keys at a time.
+// LDS image of one key tile: kIxTile rows of D FP8 bytes, 16-byte chunks XOR-swizzled per row
+// (the direct loads write 1 KiB contiguous pieces, so the swizzle is applied to which global
+// chunk each lane fetches), followed by the tile's kIxTile key scales.
+template <int D>
+struct IxTile {
+    static constexpr int CH = D / 16;                    // chunks per key row
+    static constexpr int ROWS_PER_INSTR = 64 / CH;
+    static constexpr int KEY_INSTRS = kIxTile * D / 1024;
+    static constexpr int KEY_BYTES = kIxTile * D;
+    static constexpr int BYTES = KEY_BYTES + kIxTile * 4;
+    static constexpr int SCALE_INSTRS = kIxTile / 64;    // 4-byte loads of the key scales
+    static constexpr int INSTRS = KEY_INSTRS + SCALE_INSTRS;
+    static constexpr int PER_WAVE = (INSTRS + kIxWaves - 1) / kIxWaves;
+    // 16 consecutive rows read at one logical chunk fall in distinct 16-byte bank groups.
+    __device__ static __forceinline__ int swz(int r) { return (r >> 1) & (CH - 1); }
+    __device__ static __forceinline__ int chunk(int r, int c) { return r * D + 16 * (c ^ swz(r)); }
+};
+
+// One workgroup scores kIxTokens consecutive query rows of one sequence against one segment
+// of kIxSeg keys.  The segment streams through LDS one kIxTile-key tile at a time with direct
+// global->LDS loads two tiles ahead; each wave keeps the FP8 query fragments of its two tokens
+// in registers and sweeps each tile 16 keys at a time.
 template <int H, int D>
-__global__ __launch_bounds__(kPrefillThreads, 2) void indexer_prefill_kernel(
+__global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, float* __restrict__ scores,
     int64_t stride, int row0, int n_rows, int pos0, int kbase) {
+    using T = IxTile<D>;
     constexpr int NMT = (H + 15) / 16;  // 16-head M tiles per token
     constexpr int KGRP = D / 32;        // 32-byte K groups that carry data (D = 32 or 128)
-    constexpr int KPITCH = D + 16;      // LDS bytes per key row (padding spreads banks)
     static_assert(D % 32 == 0 && D <= 128, "indexer head dim must be 32..128 in steps of 32");
-    __shared__ __attribute__((aligned(16))) uint8_t lk[kPrefillKeys * KPITCH];
-    __shared__ float lks[kPrefillKeys];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kIxBufs * T::BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;
     const int grp = lane >> 4;
 
-    const int i_first = blockIdx.x * kPrefillTokens;
+    const int i_first = blockIdx.x * kIxTokens;
     if (i_first >= n_rows) return;
-    const int i_last = min(n_rows, i_first + kPrefillTokens) - 1;
-    const int k0 = blockIdx.y * kPrefillKeys;
+    const int i_last = min(n_rows, i_first + kIxTokens) - 1;
+    const int seg0 = blockIdx.y * kIxSeg;
     const int pmax = pos0 + i_last;
-    if (k0 > pmax) return;  // tile entirely above the causal diagonal
-    const int kend = min(k0 + kPrefillKeys, pmax + 1);
-    const int nk = kend - k0;
-    const int nk16 = (nk + 15) & ~15;
-
-    // Stage the key span: 16-byte pieces, zero rows past the causal end of the tile.
-    constexpr int PIECES = D / 16;
-    for (int e = tid; e < nk16 * PIECES; e += kPrefillThreads) {
-        const int r = e / PIECES, c = e % PIECES;
-        v4i val = {0, 0, 0, 0};
-        if (r < nk) val = *(const v4i*)(k8 + (int64_t)(kbase + k0 + r) * D + c * 16);
-        *(v4i*)(lk + r * KPITCH + c * 16) = val;
-    }
-    for (int r = tid; r < nk16; r += kPrefillThreads) lks[r] = r < nk ? ks[kbase + k0 + r] : 0.f;
+    if (seg0 > pmax) return;  // segment entirely above the causal diagonal
+    const int seg_end = min(seg0 + kIxSeg, pmax + 1);
+    const int ntiles = (seg_end - seg0 + kIxTile - 1) / kIxTile;
 
     // Query fragments and folded head weights of this wave's two tokens.
     v8i qa[2][NMT];
@@ -106,39 +117,153 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void indexer_prefill_kernel(
             }
         }
     }
-    __syncthreads();
-
     const int tmax = max(tpos[0], tpos[1]);
-    if (tmax < k0) return;
-    const int ngroups = (min(kend, tmax + 1) - k0 + 15) >> 4;
-    for (int g = 0; g < ngroups; ++g) {
-        // k-groups past the head dim carry zeros in A and must carry zeros in B as well:
-        // 0 * (a stray NaN code) would poison the whole column.
+
+    // Direct loads of tile t into its ring buffer: instruction I < KEY_INSTRS moves rows
+    // I*ROWS_PER_INSTR.., the others 64 key scales each.  Rows past the causal end of the
+    // segment read the last valid key instead (their scores are never stored).
+    const uint8_t* kseq = k8 + (int64_t)kbase * D;
+    const float* sseq = ks + kbase;
+    const uint32_t lds0 = lds_addr(lds);
+    auto buf_of = [&](int t) {
+        return (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(t % kIxBufs) * T::BYTES);
+    };
+    auto issue_tile = [&](int t) {
+        const uint32_t buf = buf_of(t);
+        const int key0 = seg0 + t * kIxTile;
+#pragma unroll
+        for (int k = 0; k < T::PER_WAVE; ++k) {
+            const int I = wv + kIxWaves * k;
+            if (I < T::KEY_INSTRS) {
+                const int r = I * T::ROWS_PER_INSTR + lane / T::CH;
+                const int p = lane % T::CH;
+                const int key = min(key0 + r, pmax);
+                dma16(kseq, (uint32_t)key * D + 16 * (p ^ T::swz(r)), buf + I * 1024);
+            } else if (I < T::INSTRS) {
+                const int j = I - T::KEY_INSTRS;
+                const int key = min(key0 + 64 * j + lane, pmax);
+                dma4(sseq, (uint32_t)key * 4, buf + T::KEY_BYTES + 256 * j);
+            }
+        }
+    };
+    // Loads this wave issues per tile (the same for every tile), for the waits.
+    const int my_loads = (T::INSTRS - wv + kIxWaves - 1) / kIxWaves;
+
+    auto load_b = [&](uint32_t buf, int g) {
         v8i b = {0, 0, 0, 0, 0, 0, 0, 0};
         if (grp < KGRP) {
-            const uint8_t* bp = lk + (16 * g + col) * KPITCH + grp * 32;
-            const v4i blo = *(const v4i*)bp;
-            const v4i bhi = *(const v4i*)(bp + 16);
+            const int r = 16 * g + col;
+            const v4i blo = lds_read16(buf + T::chunk(r, 2 * grp));
+            const v4i bhi = lds_read16(buf + T::chunk(r, 2 * grp + 1));
             b = (v8i){blo.x, blo.y, blo.z, blo.w, bhi.x, bhi.y, bhi.z, bhi.w};
         }
-        v4f acc[2][NMT];
+        return b;
+    };
+    // ReLU of an MFMA output: med3(x, 0, +inf) = max(x, 0) for the finite dot products here,
+    // without the input quieting that fmaxf costs.
+    auto relu = [](float x) { return __builtin_amdgcn_fmed3f(x, 0.f, INFINITY); };
+    // Scores of a tile are held in registers and stored at the start of the next tile, after
+    // its wait: stores issued between the direct loads would otherwise lengthen the waits
+    // (they count on the same counter).  Slot s holds key groups 2s and 2s+1: lane group r
+    // keeps group 2s + (r & 1) of token r >> 1, so each store instruction writes 64 scores.
+    float held[8];
+    int held_key0 = 0, held_groups = 0;
+    auto flush = [&]() {
+        const int g_odd = grp & 1, tok = grp >> 1;
+        const int my_pos = tok ? tpos[1] : tpos[0];
+        const int64_t my_row = tok ? trow[1] : trow[0];
+#pragma unroll
+        for (int slot = 0; slot < 8; ++slot) {
+            const int g = 2 * slot + g_odd;
+            const int s = held_key0 + 16 * g + col;
+            if (g < held_groups && s <= my_pos) scores[my_row * stride + s] = held[slot];
+        }
+        held_groups = 0;
+    };
+    // Weighted ReLU sum over this lane's 16 heads of each token (the head sum is finished by
+    // reduce_pair across the four lane groups).
+    auto head_partials = [&](const v4f (&acc)[2][NMT], float (&part)[2]) {
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {
+            float p = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p = fmaf(wt[tok][mt][r], relu(acc[tok][mt][r]), p);
+            part[tok] = p;
+        }
+    };
+    // Sums the partials of groups 2s (pe) and 2s+1 (po) over the four lane groups with two
+    // lane-swap rounds, leaving lane group r with group 2s + (r & 1) of token r >> 1 (the
+    // layout flush expects), then applies that key's scale.
+    auto reduce_pair = [&](const float (&pe)[2], const float (&po)[2], uint32_t buf, int slot) {
+        auto sw32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe[0]), __float_as_uint(pe[1]), false, false);
+        auto sw32o = __builtin_amdgcn_permlane32_swap(__float_as_uint(po[0]), __float_as_uint(po[1]), false, false);
+        const float x = __uint_as_float(sw32[0]) + __uint_as_float(sw32[1]);
+        const float y = __uint_as_float(sw32o[0]) + __uint_as_float(sw32o[1]);
+        auto sw16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        const float z = __uint_as_float(sw16[0]) + __uint_as_float(sw16[1]);
+        const float kscale = *(const __attribute__((address_space(3))) float*)(size_t)(
+            buf + T::KEY_BYTES + 4 * (16 * (2 * slot + (grp & 1)) + col));
+        held[slot] = z * kscale;
+    };
+    auto mfmas = [&](v4f (&acc)[2][NMT], const v8i& b) {
 #pragma unroll
         for (int tok = 0; tok < 2; ++tok)
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], b);
-        const int s = k0 + 16 * g + col;
-        const float kscale = lks[16 * g + col];
-#pragma unroll
-        for (int tok = 0; tok < 2; ++tok) {
-            float part = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) part += wt[tok][mt][r] * fmaxf(acc[tok][mt][r], 0.f);
-            part = sum_over_groups(part);
-            if (grp == 0 && s <= tpos[tok]) scores[(int64_t)trow[tok] * stride + s] = part * kscale;
+    };
+
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int t = 0; t < ntiles; ++t) {
+        // Tile t has landed for this wave (the younger loads of tile t+1 may still fly; the
+        // stores issued since are older than nothing we wait for), then for every wave; the
+        // barrier also retires tile t-1, whose buffer tile t+2 takes over.
+        if (t + 1 < ntiles) {
+            if (my_loads == 5) wait_loads<5>();
+            else if (my_loads == 4) wait_loads<4>();
+            else if (my_loads == 3) wait_loads<3>();
+            else if (my_loads == 2) wait_loads<2>();
+            else if (my_loads == 1) wait_loads<1>();
+            else wait_loads<0>();
+        } else {
+            wait_loads<0>();
         }
+        lds_barrier();
+        flush();  // scores of tile t-1, before the loads of tile t+2
+        if (t + 2 < ntiles) issue_tile(t + 2);
+        const int key0 = seg0 + t * kIxTile;
+        if (key0 > tmax) continue;  // this wave's tokens are all before the tile
+        const uint32_t buf = buf_of(t);
+        const int ngroups = min(kIxTile / 16, (tmax - key0) / 16 + 1);
+
+        // The two waves of a SIMD overlap one's epilogue with the other's MFMAs; within a wave
+        // the operand reads fly two groups ahead.  Fully unrolled so the held slots and the
+        // operand registers are static.
+        v8i bq[2];
+        bq[0] = load_b(buf, 0);
+        if (ngroups > 1) bq[1] = load_b(buf, 1);
+#pragma unroll
+        for (int slot = 0; slot < kIxTile / 32; ++slot) {
+            if (2 * slot < ngroups) {
+                float pe[2], po[2] = {0.f, 0.f};
+                v4f acc[2][NMT];
+                mfmas(acc, bq[0]);
+                if (2 * slot + 2 < ngroups) bq[0] = load_b(buf, 2 * slot + 2);
+                head_partials(acc, pe);
+                if (2 * slot + 1 < ngroups) {
+                    mfmas(acc, bq[1]);
+                    if (2 * slot + 3 < ngroups) bq[1] = load_b(buf, 2 * slot + 3);
+                    head_partials(acc, po);
+                }
+                reduce_pair(pe, po, buf, slot);
+            }
+        }
+        held_key0 = key0;
+        held_groups = ngroups;
     }
+    flush();
 }
 
 constexpr int kDecodeThreads = 256;
@@ -230,8 +355,8 @@ hipError_t launch_prefill_t(const IndexerArgs& a, int row0, int n_rows, int pos0
                             float* scores, hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
     const int pmax = pos0 + n_rows - 1;
-    dim3 grid((n_rows + kPrefillTokens - 1) / kPrefillTokens, pmax / kPrefillKeys + 1);
-    hipLaunchKernelGGL((indexer_prefill_kernel<H, D>), grid, dim3(kPrefillThreads), 0, st, a.q8,
+    dim3 grid((n_rows + kIxTokens - 1) / kIxTokens, pmax / kIxSeg + 1);
+    hipLaunchKernelGGL((indexer_prefill_kernel<H, D>), grid, dim3(kIxThreads), 0, st, a.q8,
                        a.q_scale, a.w, a.k8, a.k_scale, scores, a.score_stride, row0, n_rows,
                        pos0, kbase);
     return hipGetLastError();

@@ -90,27 +90,6 @@ __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
-
-typedef __attribute__((address_space(3))) v4i lds_v4i;
-
-// LDS accesses by 32-bit LDS byte address (a uniform buffer base plus a per-lane offset, so a
-// read costs one add and constant parts ride in the instruction's offset field).
-__device__ __forceinline__ v4s ds_read_tr16(uint32_t a) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(size_t)a);
-}
-__device__ __forceinline__ v4i lds_read16(uint32_t a) { return *(const lds_v4i*)(size_t)a; }
-__device__ __forceinline__ void lds_write16(uint32_t a, v4i v) { *(lds_v4i*)(size_t)a = v; }
-
-// Workgroup barrier that orders LDS accesses only: in-flight direct global->LDS loads into
-// the other buffers are not waited for (the fence of a full __syncthreads would drain them).
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");  // no LDS access moves above the barrier
-}
-
 // Keeps an MFMA accumulator tile in AGPRs across a join of control flow, so that the register
 // allocator does not route the loop-carried tile through VGPRs on every iteration.
 __device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); }
@@ -132,10 +111,6 @@ __device__ __forceinline__ void scale_agpr(v16f& x, float alpha) {
             : "v"(alpha));
         x[r] = e;
     }
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Reads the two halves' partial logit tiles (4 x 16 bytes each, 1 KiB apart) and waits for
@@ -182,23 +157,6 @@ __device__ __forceinline__ void piece_of(int I, int lane, int& r, int& col, int&
     base = rope ? RV::BYTES + Ir * 1024 : Ir * 1024;
 }
 
-// One direct global->LDS load of 16 bytes per lane from kvb + off: lane i's bytes land at
-// lds_base + 16 * i.  Issued from asm so that the compiler's wait-count bookkeeping does not
-// see it: as a FLAT access that touches LDS it would otherwise turn every later LDS wait into
-// a full drain.  Completion is tracked by hand with wait_loads (the load counts on vmcnt only)
-// and a barrier before any other wave reads the bytes.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber still orders it
-__device__ __forceinline__ void dma16(const uint8_t* kvb, uint32_t off, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2"
-        :
-        : "s"(lds_base), "v"(off), "s"(kvb)
-        : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Issues the direct global->LDS loads of one block of kBlk latent rows into the buffer at
 // LDS address `buf`; `offs` points at the block's kBlk row byte offsets in LDS (empty slots
@@ -247,11 +205,6 @@ __device__ __forceinline__ void zero_empty_rows(uint32_t buf, uint32_t vmask, in
     }
 }
 
-// Waits until at most N direct loads of this wave are still in flight (they complete in order).
-template <int N>
-__device__ __forceinline__ void wait_loads() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <int H, int DQK, int DV, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
