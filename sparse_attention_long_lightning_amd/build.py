@@ -50,7 +50,8 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"
-    _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
+    # --no-undefined: a kernel whose host stub was not emitted fails here, not at load time
+    _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

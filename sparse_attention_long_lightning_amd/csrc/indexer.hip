@@ -24,6 +24,17 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
 }
 
+// Forces a loaded value to be present in registers at this point of the program.
+__device__ __forceinline__ void materialize(const v8i& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void materialize(float x) { asm volatile("" ::"v"(x)); }
+
+// p + w * ReLU(x) as two FMAs, using ReLU(x) = (x + |x|) / 2 with the 1/2 folded into w:
+// max-based forms cost an extra instruction to quiet the MFMA output first.  The two terms
+// cancel to within fp32 rounding of |w x| for x < 0, far below the FP8 products' own error.
+__device__ __forceinline__ float fma_relu_half(float w_half, float x, float p) {
+    return fmaf(w_half, fabsf(x), fmaf(w_half, x, p));
+}
+
 // Sum over the four 16-lane groups; every lane ends with the total of its column.
 __device__ __forceinline__ float sum_over_groups(float v) {
     v += __shfl_xor(v, 16);
@@ -87,7 +98,9 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
     const int seg_end = min(seg0 + kIxSeg, pmax + 1);
     const int ntiles = (seg_end - seg0 + kIxTile - 1) / kIxTile;
 
-    // Query fragments and folded head weights of this wave's two tokens.
+    // Query fragments and folded head weights of this wave's two tokens.  Every load is
+    // issued unconditionally from a clamped (valid) address and masked afterwards, so they
+    // all fly together instead of one branch-guarded round trip at a time.
     v8i qa[2][NMT];
     float wt[2][NMT][4];
     int tpos[2];
@@ -102,22 +115,32 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
             const int h = mt * 16 + col;
-            v8i a = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (ok && h < H && grp < KGRP) {
-                const uint8_t* src = q8 + (qrow * H + h) * D + grp * 32;
-                const v4i lo = *(const v4i*)src;
-                const v4i hi = *(const v4i*)(src + 16);
-                a = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            }
-            qa[tok][mt] = a;
+            const bool qv = ok && h < H && grp < KGRP;
+            const uint8_t* src = q8 + (qrow * H + min(h, H - 1)) * D + min(grp, KGRP - 1) * 32;
+            const v4i lo = *(const v4i*)src;
+            const v4i hi = *(const v4i*)(src + 16);
+            const v8i a = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            qa[tok][mt] = qv ? a : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int hh = mt * 16 + grp * 4 + r;
-                wt[tok][mt][r] = (ok && hh < H) ? w[qrow * H + hh] * qs[qrow * H + hh] : 0.f;
+                const int64_t e = qrow * H + min(hh, H - 1);
+                const float v = 0.5f * w[e] * qs[e];  // halved for fma_relu_half
+                wt[tok][mt][r] = (ok && hh < H) ? v : 0.f;
             }
         }
     }
     const int tmax = max(tpos[0], tpos[1]);
+    // The query loads complete here, before any direct load is issued: a wait for them placed
+    // by the compiler inside the tile loop would also drain the direct loads in flight.
+#pragma unroll
+    for (int tok = 0; tok < 2; ++tok)
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+            materialize(qa[tok][mt]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) materialize(wt[tok][mt][r]);
+        }
 
     // Direct loads of tile t into its ring buffer: instruction I < KEY_INSTRS moves rows
     // I*ROWS_PER_INSTR.., the others 64 key scales each.  Rows past the causal end of the
@@ -159,9 +182,6 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         }
         return b;
     };
-    // ReLU of an MFMA output: med3(x, 0, +inf) = max(x, 0) for the finite dot products here,
-    // without the input quieting that fmaxf costs.
-    auto relu = [](float x) { return __builtin_amdgcn_fmed3f(x, 0.f, INFINITY); };
     // Scores of a tile are held in registers and stored at the start of the next tile, after
     // its wait: stores issued between the direct loads would otherwise lengthen the waits
     // (they count on the same counter).  Slot s holds key groups 2s and 2s+1: lane group r
@@ -189,7 +209,7 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p = fmaf(wt[tok][mt][r], relu(acc[tok][mt][r]), p);
+                for (int r = 0; r < 4; ++r) p = fma_relu_half(wt[tok][mt][r], acc[tok][mt][r], p);
             part[tok] = p;
         }
     };
@@ -238,27 +258,68 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         const uint32_t buf = buf_of(t);
         const int ngroups = min(kIxTile / 16, (tmax - key0) / 16 + 1);
 
-        // The two waves of a SIMD overlap one's epilogue with the other's MFMAs; within a wave
-        // the operand reads fly two groups ahead.  Fully unrolled so the held slots and the
-        // operand registers are static.
+        // The eight MFMAs of a group (token-major: k = 4*tok + mt) each run with the epilogue
+        // FMAs of the MFMA issued just before them, so the matrix pipe stays busy while the VALU
+        // works on a result that is already there; the last MFMA of a group is taken up under
+        // the first of the next.  Operand reads fly two groups ahead.  Fully unrolled so held
+        // slots, accumulators and operand registers are static; program order is pinned with
+        // scheduling barriers.
+        constexpr int NG = kIxTile / 16;
+        constexpr int NK = 2 * NMT;
         v8i bq[2];
+        v4f acc[2][NMT];
+        float part[2][2];  // [group parity][token]
         bq[0] = load_b(buf, 0);
         if (ngroups > 1) bq[1] = load_b(buf, 1);
+        // epilogue FMAs of MFMA k of group gg
+        auto epi_k = [&](int gg, int k) {
+            const int tok = k / NMT, mt = k % NMT;
+            float p = mt == 0 ? 0.f : part[gg & 1][tok];
 #pragma unroll
-        for (int slot = 0; slot < kIxTile / 32; ++slot) {
-            if (2 * slot < ngroups) {
-                float pe[2], po[2] = {0.f, 0.f};
-                v4f acc[2][NMT];
-                mfmas(acc, bq[0]);
-                if (2 * slot + 2 < ngroups) bq[0] = load_b(buf, 2 * slot + 2);
-                head_partials(acc, pe);
-                if (2 * slot + 1 < ngroups) {
-                    mfmas(acc, bq[1]);
-                    if (2 * slot + 3 < ngroups) bq[1] = load_b(buf, 2 * slot + 3);
-                    head_partials(acc, po);
-                }
-                reduce_pair(pe, po, buf, slot);
+            for (int r = 0; r < 4; ++r) p = fma_relu_half(wt[tok][mt][r], acc[tok][mt][r], p);
+            part[gg & 1][tok] = p;
+        };
+        // groups 2s and 2s+1 (or a lone last group) are complete: reduce them into slot s
+        auto close_group = [&](int gg) {
+            if (gg & 1) {
+                reduce_pair(part[0], part[1], buf, gg >> 1);
+            } else if (gg == ngroups - 1) {
+                const float zero[2] = {0.f, 0.f};
+                reduce_pair(part[0], zero, buf, gg >> 1);
             }
+        };
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g < ngroups) {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) {
+                    const int tok = k / NMT, mt = k % NMT;
+                    if (k > 0) {
+                        acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], bq[g & 1]);
+                        epi_k(g, k - 1);
+                    } else {
+                        // MFMA 0 overwrites acc[0][0], already consumed; the previous group's
+                        // last MFMA result is taken up now
+                        acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], bq[g & 1]);
+                        if (g > 0) {
+                            epi_k(g - 1, NK - 1);
+                            close_group(g - 1);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (g + 2 < ngroups) bq[g & 1] = load_b(buf, g + 2);
+            }
+        }
+        // the last group's last MFMA
+        {
+            const int gl = ngroups - 1;
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg)
+                if (gg == gl) {
+                    epi_k(gg, NK - 1);
+                    close_group(gg);
+                }
         }
         held_key0 = key0;
         held_groups = ngroups;
