@@ -261,66 +261,44 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         // The eight MFMAs of a group (token-major: k = 4*tok + mt) each run with the epilogue
         // FMAs of the MFMA issued just before them, so the matrix pipe stays busy while the VALU
         // works on a result that is already there; the last MFMA of a group is taken up under
-        // the first of the next.  Operand reads fly two groups ahead.  Fully unrolled so held
-        // slots, accumulators and operand registers are static; program order is pinned with
-        // scheduling barriers.
+        // the first of the next.  Operand reads fly two groups ahead.  Every group of the tile
+        // is computed (rows past the causal end hold valid clamped keys; their scores are not
+        // stored), so the fully unrolled sequence has no branches and the held slots,
+        // accumulators and operand registers stay static.
         constexpr int NG = kIxTile / 16;
         constexpr int NK = 2 * NMT;
         v8i bq[2];
         v4f acc[2][NMT];
         float part[2][2];  // [group parity][token]
         bq[0] = load_b(buf, 0);
-        if (ngroups > 1) bq[1] = load_b(buf, 1);
-        // epilogue FMAs of MFMA k of group gg
-        auto epi_k = [&](int gg, int k) {
+        bq[1] = load_b(buf, 1);
+        auto epi_k = [&](int gg, int k) {  // epilogue FMAs of MFMA k of group gg
             const int tok = k / NMT, mt = k % NMT;
             float p = mt == 0 ? 0.f : part[gg & 1][tok];
 #pragma unroll
             for (int r = 0; r < 4; ++r) p = fma_relu_half(wt[tok][mt][r], acc[tok][mt][r], p);
             part[gg & 1][tok] = p;
         };
-        // groups 2s and 2s+1 (or a lone last group) are complete: reduce them into slot s
-        auto close_group = [&](int gg) {
-            if (gg & 1) {
-                reduce_pair(part[0], part[1], buf, gg >> 1);
-            } else if (gg == ngroups - 1) {
-                const float zero[2] = {0.f, 0.f};
-                reduce_pair(part[0], zero, buf, gg >> 1);
-            }
-        };
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            if (g < ngroups) {
 #pragma unroll
-                for (int k = 0; k < NK; ++k) {
-                    const int tok = k / NMT, mt = k % NMT;
-                    if (k > 0) {
-                        acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], bq[g & 1]);
-                        epi_k(g, k - 1);
-                    } else {
-                        // MFMA 0 overwrites acc[0][0], already consumed; the previous group's
-                        // last MFMA result is taken up now
-                        acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], bq[g & 1]);
-                        if (g > 0) {
-                            epi_k(g - 1, NK - 1);
-                            close_group(g - 1);
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+            for (int k = 0; k < NK; ++k) {
+                const int tok = k / NMT, mt = k % NMT;
+                // MFMA k overwrites acc[k], whose previous contents were consumed a step ago
+                acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], bq[g & 1]);
+                if (k > 0) {
+                    epi_k(g, k - 1);
+                } else if (g > 0) {
+                    epi_k(g - 1, NK - 1);  // the previous group is complete
+                    if (g & 1) continue;
+                    reduce_pair(part[0], part[1], buf, (g - 1) >> 1);
                 }
-                if (g + 2 < ngroups) bq[g & 1] = load_b(buf, g + 2);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            if (g + 2 < NG) bq[g & 1] = load_b(buf, g + 2);
         }
-        // the last group's last MFMA
-        {
-            const int gl = ngroups - 1;
-#pragma unroll
-            for (int gg = 0; gg < NG; ++gg)
-                if (gg == gl) {
-                    epi_k(gg, NK - 1);
-                    close_group(gg);
-                }
-        }
+        epi_k(NG - 1, NK - 1);
+        reduce_pair(part[0], part[1], buf, (NG - 1) >> 1);
         held_key0 = key0;
         held_groups = ngroups;
     }
