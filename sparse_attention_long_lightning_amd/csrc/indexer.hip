@@ -272,12 +272,22 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         float part[2][2];  // [group parity][token]
         bq[0] = load_b(buf, 0);
         bq[1] = load_b(buf, 1);
-        auto epi_k = [&](int gg, int k) {  // epilogue FMAs of MFMA k of group gg
+        // Epilogue FMAs of MFMA k of group gg, as two independent chains (the x terms and the
+        // |x| terms) so consecutive FMAs do not wait on each other.
+        float lin[2][2], mag[2][2];  // [group parity][token]
+        auto epi_k = [&](int gg, int k) {
             const int tok = k / NMT, mt = k % NMT;
-            float p = mt == 0 ? 0.f : part[gg & 1][tok];
+            float a = mt == 0 ? 0.f : lin[gg & 1][tok];
+            float m = mt == 0 ? 0.f : mag[gg & 1][tok];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p = fma_relu_half(wt[tok][mt][r], acc[tok][mt][r], p);
-            part[gg & 1][tok] = p;
+            for (int r = 0; r < 4; ++r) {
+                a = fmaf(wt[tok][mt][r], acc[tok][mt][r], a);
+                m = fmaf(wt[tok][mt][r], fabsf(acc[tok][mt][r]), m);
+            }
+            asm volatile("" : "+v"(a), "+v"(m));  // keep these FMAs in this step
+            lin[gg & 1][tok] = a;
+            mag[gg & 1][tok] = m;
+            if (mt == NMT - 1) part[gg & 1][tok] = a + m;
         };
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -293,6 +303,8 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
                     if (g & 1) continue;
                     reduce_pair(part[0], part[1], buf, (g - 1) >> 1);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // the MFMA first,
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then the FMAs
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (g + 2 < NG) bq[g & 1] = load_b(buf, g + 2);
