@@ -42,8 +42,8 @@ __device__ __forceinline__ float sum_over_groups(float v) {
     return v;
 }
 
-constexpr int kIxTokens = 16;    // query tokens per workgroup (2 per wave)
-constexpr int kIxThreads = 512;  // 8 waves: two per SIMD, so one wave's epilogue runs under
+constexpr int kIxTokens = 24;    // query tokens per workgroup (2 per wave)
+constexpr int kIxThreads = 768;  // 12 waves: three per SIMD, so one wave's epilogue runs under
                                  // the other's MFMAs
 constexpr int kIxWaves = kIxThreads / kWave;
 constexpr int kIxTile = 256;     // keys per LDS tile
