@@ -57,7 +57,7 @@ struct Region {
 
 template <int H, int DQK, int DV>
 struct MqaCfg {
-    static constexpr int THREADS = 256;        // 4 waves: 2 head groups x 2 halves
+    static constexpr int THREADS = 512;        // 4 logit waves + 4 value waves (2 groups x 2 halves)
     static constexpr int NW = 4;
     static constexpr int NHH = (H + 63) / 64;  // workgroups per query row, 64 heads each
     static constexpr int KS = DQK / 16;        // k-slices of the logit product
@@ -113,26 +113,6 @@ __device__ __forceinline__ void scale_agpr(v16f& x, float alpha) {
     }
 }
 
-// Reads the two halves' partial logit tiles (4 x 16 bytes each, 1 KiB apart) and waits for
-// them inside the same asm block.  Written as asm so that the compiler does not treat these
-// LDS reads as possibly aliasing the in-flight direct loads of later blocks (it would drain
-// them with a vmcnt(0) wait); nothing is left in flight when the block ends.
-__device__ __forceinline__ void read_partials(uint32_t a0, uint32_t b0, v4f a[4], v4f b[4]) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n"
-        "ds_read_b128 %1, %8 offset:1024\n"
-        "ds_read_b128 %2, %8 offset:2048\n"
-        "ds_read_b128 %3, %8 offset:3072\n"
-        "ds_read_b128 %4, %9\n"
-        "ds_read_b128 %5, %9 offset:1024\n"
-        "ds_read_b128 %6, %9 offset:2048\n"
-        "ds_read_b128 %7, %9 offset:3072\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]),
-          "=&v"(b[3])
-        : "v"(a0), "v"(b0)
-        : "memory");
-}
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
     __bf16 b = (__bf16)x;
@@ -207,7 +187,7 @@ __device__ __forceinline__ void zero_empty_rows(uint32_t buf, uint32_t vmask, in
 
 
 template <int H, int DQK, int DV, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
+__global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     int topk, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float2* __restrict__ part_ml, RowMap map, int n_rows, int n_split, float sm_log2) {
@@ -218,6 +198,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     __shared__ uint32_t lofs[kMaxTopk];            // byte offset of each selected row (0 if empty)
     __shared__ uint32_t lmask[kMaxTopk / kBlk];    // per block: bit j = slot j holds a row
     __shared__ __attribute__((aligned(16))) float sx[2][2][4][kWave][4];  // [group][half][r/4][lane][r%4]
+    __shared__ __attribute__((aligned(16))) v4i pbuf[2][2][2][kWave];     // P^T: [parity][group][slice][lane]
+    __shared__ float abuf[2][2][32];   // O rescale factor: [parity][group][head]
+    __shared__ float lfin[2][2][32];   // final row sums: [group][half][head]
+    __shared__ float mfin[2][32];      // final running max: [group][head]
 
     // Work item.  With two workgroups per row (64 heads each) the pair is issued 8 ids
     // apart, i.e. onto the same XCD, so the second gather of each latent row hits its L2.
@@ -234,8 +218,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     const int split = SPLIT ? blockIdx.y : 0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
-    const int hg = wv & 1;  // head group: 32 heads
-    const int dp = wv >> 1;  // half: logit dims and value tiles
+    const bool logit_wave = wv < 4;  // waves 0-3: logits and softmax; 4-7: value product
+    const int w4 = wv & 3;
+    const int hg = w4 & 1;  // head group: 32 heads
+    const int dp = w4 >> 1;  // half: of the logit dims (logit waves) or value tiles (value waves)
     const RowInfo ri = row_info(map, row);
     const int per = SPLIT ? (((topk + n_split - 1) / n_split + kBlk - 1) / kBlk) * kBlk : topk;
     const int j0 = split * per;
@@ -243,67 +229,11 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     const int nblk = j1 > j0 ? (j1 - j0 + kBlk - 1) / kBlk : 0;
     const int32_t* irow = idx + (int64_t)row * topk;
     const uint8_t* kvb = (const uint8_t*)(kv + (int64_t)ri.kbase * DQK);
-
-    // Logit k-slices of this wave's half: value slices dp*KSV2 + i (i < KSV2), then rope
-    // slices KSV + dp*RH + j.  Lane l holds head 64*hh + 32*hg + l%32, dims 8*(l/32) .. +7 of
-    // each slice.
     const int head = hh * 64 + hg * 32 + (lane & 31);
     const int half = lane >> 5;
-    const int nrope = min(C::RH, C::R - dp * C::RH);  // rope slices of this half
-    const int nks = C::KSV2 + nrope;
-    v8bf qf[C::KS0];
-    {
-        const uint16_t* qp = q + ((int64_t)ri.qrow * H + (head < H ? head : 0)) * DQK + 8 * half;
-#pragma unroll
-        for (int i = 0; i < C::KS0; ++i) {
-            const int ks = i < C::KSV2 ? dp * C::KSV2 + i : C::KSV + dp * C::RH + (i - C::KSV2);
-            v4i v = {0, 0, 0, 0};
-            if (head < H && i < nks) v = *(const v4i*)(qp + 16 * ks);
-            qf[i] = __builtin_bit_cast(v8bf, v);
-            pin_agpr(qf[i]);
-        }
-    }
-
-    v16f oacc[C::VT0];
-#pragma unroll
-    for (int vt = 0; vt < C::VT0; ++vt) oacc[vt] = (v16f){};
-    float m_run = -INFINITY;  // running max of the base-2 logits of this lane's head
-    float l_run = 0.f;        // running sum over this lane's half of the block rows
-
-    // Block row held by MFMA row i = l%32 of the logit product: lanes of each 32-lane half
-    // must own 8 consecutive block rows per 16-row k-slice of the value product.
     const int mi = lane & 31;
-    const int srow = 16 * (mi >> 4) + 8 * ((mi >> 2) & 1) + 4 * ((mi >> 3) & 1) + (mi & 3);
     const int j16 = lane & 15;
-
-    // Per-lane LDS offsets within a block buffer.
-    //  logit operand of value slice i: qoff[i % TLQ] + 32*TLQ*(i / TLQ);
-    //  logit operand of rope slice j:  roff[j];
-    //  value operand (tr16 read) of 16-row slice u, row quad h, tile t:
-    //      voff[u][h][t % TLV] + 64*TLV*(t / TLV).
-    // tr16 source lane j of each 16-lane group points at block row 16u + 8*half + j/4 (+4 for
-    // h = 1) and value columns cl*8 + sub/2 .. +3 of the tile.
-    uint32_t qoff[C::TLQ], roff[C::RH], voff[2][2][C::TLV];
-#pragma unroll
-    for (int i = 0; i < C::TLQ; ++i) qoff[i] = RV::chunk(srow, dp * C::KSV + 2 * i + half);
-#pragma unroll
-    for (int j = 0; j < C::RH; ++j) roff[j] = RV::BYTES + RR::chunk(srow, 2 * (dp * C::RH + j) + half);
-    {
-        const int vsub = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);  // value column of this tr16 lane
-        const int cl = vsub >> 3, sub = (vsub & 7) * 2;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int t = 0; t < C::TLV; ++t)
-                    voff[u][h][t] = RV::chunk(16 * u + 8 * half + (j16 >> 2) + 4 * h,
-                                              4 * (dp * C::VT0 + t) + cl) + sub;
-    }
     const uint32_t lds0 = lds_addr(lds);
-    const uint32_t sx_own = lds_addr(&sx[hg][dp][0][lane][0]);
-    const uint32_t sx0 = lds_addr(&sx[hg][0][0][lane][0]);
-    const uint32_t sx1 = lds_addr(&sx[hg][1][0][lane][0]);
 
     // Selected rows of the work item, staged in LDS once: byte offsets (row 0 for an empty
     // slot) and per-block occupancy masks.  A row's offset must fit in 31 bits.
@@ -322,10 +252,6 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
     auto buf_of = [&](int blk) {
         return (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(blk % 3) * C::BUF);
     };
-    auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
-        const uint32_t vm = lmask[blk];
-        if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, wv, lane);
-    };
     // Per-lane addresses base + off, made opaque so that constant parts added afterwards go
     // into the instructions' offset field instead of into one add per read.
     auto opaque = [](uint32_t x) {
@@ -333,146 +259,249 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
         return x;
     };
 
-    // ---- phase pieces ----
-    // Logit operand of slice i of this wave's half (value slices, then rope slices).
-    auto qk_read = [&](const uint32_t (&qa)[C::TLQ], const uint32_t (&ra)[C::RH], int i) {
-        if (i < C::KSV2) return lds_read16(qa[i % C::TLQ] + 32 * C::TLQ * (i / C::TLQ));
-        return lds_read16(ra[i - C::KSV2]);
-    };
-    // p = 2^(sm_log2 * z - m_run) of element e; masked rows (z = -inf) give exact zeros,
-    // also while no row has been seen (m_run = -inf is then replaced by 0).
-    // The empty asm anchors each result at its place in the fixed program order (plain
-    // arithmetic would otherwise be sunk past the scheduling barriers to its first use).
-    auto exp_elem = [&](const float (&zc)[16], int e, float mref, float (&pe)[16], float& ls) {
-        pe[e] = __builtin_amdgcn_exp2f(fmaf(zc[e], sm_log2, -mref));
-        ls += pe[e];
-        asm volatile("" : "+v"(pe[e]), "+v"(ls));
-    };
-    // Masks empty rows of a block's logits and folds them into the running max m_run (base-2
-    // units); returns the rescale factor for O and l (1 when the max did not jump by more
-    // than kRescaleGap, 0 for the first rows seen).
-    auto block_max = [&](float (&z)[16], uint32_t vmask) {
-        if (vmask != 0xffffffffu) {
+    // Pipeline over the blocks (three LDS buffers for the gathered rows, two for P^T).  Step b:
+    //   top   block b+1's loads have landed (issuing waves wait, then a barrier); P^T of block b
+    //         and its rescale factor are visible; block b-1's buffer is free
+    //   logit waves:  logit MFMAs of block b+1 with block b+2's direct loads, exchange of the
+    //                 partial logits (barrier), softmax of block b+1 -> P^T, rescale factor
+    //   value waves:  rescale O if the max moved, value MFMAs of block b (half of them before
+    //                 the exchange barrier, half after)
+    // Both kinds of wave pass the same barriers in the same order; a logit wave and a value
+    // wave share each SIMD, so one's VALU work runs under the other's MFMAs.
+    if (logit_wave) {
+        // ---------------- logits and softmax ----------------
+        // Logit k-slices of this wave's half: value slices dp*KSV2 + i (i < KSV2), then rope
+        // slices KSV + dp*RH + j.  Lane l holds head 64*hh + 32*hg + l%32, dims 8*(l/32) .. +7
+        // of each slice.
+        const int nrope = min(C::RH, C::R - dp * C::RH);
+        const int nks = C::KSV2 + nrope;
+        // Loaded unconditionally from clamped addresses and masked afterwards, so all the
+        // loads fly together; then moved to AGPRs (MFMA B operands are read from there).
+        v8bf qf[C::KS0];
+        {
+            const uint16_t* qp = q + ((int64_t)ri.qrow * H + (head < H ? head : 0)) * DQK + 8 * half;
+            v4i v[C::KS0];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
-                if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
+            for (int i = 0; i < C::KS0; ++i) {
+                const int ks = i < C::KSV2 ? dp * C::KSV2 + i : C::KSV + dp * C::RH + (i - C::KSV2);
+                v[i] = *(const v4i*)(qp + 16 * min(ks, C::KS - 1));
+            }
+#pragma unroll
+            for (int i = 0; i < C::KS0; ++i) {
+                const bool ok = head < H && i < nks;
+                qf[i] = __builtin_bit_cast(v8bf, ok ? v[i] : (v4i){0, 0, 0, 0});
+                pin_agpr(qf[i]);
             }
         }
-        // med3(a, b, +inf) = max(a, b) for the non-NaN logits here; unlike fmaxf it needs no
-        // quieting of its inputs first
-        float mb = __builtin_amdgcn_fmed3f(z[0], z[1], INFINITY);
+        float m_run = -INFINITY;  // running max of the base-2 logits of this lane's head
+        float l_run = 0.f;        // running sum over this wave's rows of this lane's head
+        // Block row held by MFMA row i = l%32 of the logit product: lanes of each 32-lane half
+        // must own 8 consecutive block rows per 16-row k-slice of the value product.
+        const int srow = 16 * (mi >> 4) + 8 * ((mi >> 2) & 1) + 4 * ((mi >> 3) & 1) + (mi & 3);
+        // Per-lane LDS offsets within a block buffer: logit operand of value slice i at
+        // qoff[i % TLQ] + 32*TLQ*(i / TLQ), of rope slice j at roff[j].
+        uint32_t qoff[C::TLQ], roff[C::RH];
 #pragma unroll
-        for (int r = 2; r < 16; ++r) mb = __builtin_amdgcn_fmed3f(mb, z[r], INFINITY);
-        mb = __builtin_amdgcn_fmed3f(mb, __shfl_xor(mb, 32), INFINITY) * sm_log2;
-        return mb;
-    };
-    auto rescale = [&](float mb) {
-        const bool bump = mb > m_run + kRescaleGap;
-        if (__ballot(bump) != 0ull) {
-            const bool fresh = m_run == -INFINITY;
-            const float m_new = bump ? mb : m_run;
-            const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-            if (__ballot(!fresh) != 0ull) {
-                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // MFMA results settle
+        for (int i = 0; i < C::TLQ; ++i) qoff[i] = RV::chunk(srow, dp * C::KSV + 2 * i + half);
 #pragma unroll
-                for (int vt = 0; vt < C::VT0; ++vt) scale_agpr(oacc[vt], alpha);
-                asm volatile("s_nop 4" ::: "memory");  // before the next MFMA reads them
-            }
-        }
-    };
+        for (int j = 0; j < C::RH; ++j) roff[j] = RV::BYTES + RR::chunk(srow, 2 * (dp * C::RH + j) + half);
+        const uint32_t sx_own = lds_addr(&sx[hg][dp][0][lane][0]);
+        const uint32_t sx_other = lds_addr(&sx[hg][1 - dp][0][lane][0]);
 
-    // Phase B of a step: S^T partial of block `nb` (next) with the logit MFMAs (when QK),
-    // while block `zc`'s exponentials (when EXP) and the direct loads of block `db` (when DMA)
-    // fill the gaps between them.  Program order is fixed with scheduling barriers; the
-    // compiler then waits for each operand read only as far as needed.
-    constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
-    constexpr int AHEAD = C::KS0 < 6 ? C::KS0 : 6;
-    auto phase_b = [&](uint32_t nb, const float (&zc)[16], v8bf (&pf)[2], int db, auto QK, auto EXP,
-                       auto DMA) -> v16f {
-        constexpr bool do_qk = decltype(QK)::value, do_exp = decltype(EXP)::value;
-        constexpr bool do_dma = decltype(DMA)::value;
-        uint32_t o[MAXK];
-        uint32_t dbuf = 0;
-        if constexpr (do_dma) {
-            dbuf = buf_of(db);
-#pragma unroll
-            for (int k = 0; k < MAXK; ++k) {
-                const int I = wv + C::NW * k;
-                int r, col, base;
-                piece_of<C>(I, lane, r, col, base);
-                o[k] = (C::INSTRS % C::NW == 0 || I < C::INSTRS) ? lofs[db * kBlk + r] + col : 0u;
-            }
-        }
-        auto dma_k = [&](int k) {
-            const int I = wv + C::NW * k;
-            if (C::INSTRS % C::NW == 0 || I < C::INSTRS) {
-                int r, col, base;
-                piece_of<C>(I, lane, r, col, base);
-                dma16(kvb, o[k], dbuf + base);
-            }
+        auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
+            const uint32_t vm = lmask[blk];
+            if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, w4, lane);
         };
-        uint32_t qa[C::TLQ], ra[C::RH];
-        v4i av[C::KS0];
-        if constexpr (do_qk) {
+        auto qk_read = [&](const uint32_t (&qa)[C::TLQ], const uint32_t (&ra)[C::RH], int i) {
+            if (i < C::KSV2) return lds_read16(qa[i % C::TLQ] + 32 * C::TLQ * (i / C::TLQ));
+            return lds_read16(ra[i - C::KSV2]);
+        };
+        // Partial S^T of block `nb` over this wave's dims, published to the other half of the
+        // head group; the direct loads of block `db` (when DMA) go out between the MFMAs.
+        constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
+        constexpr int AHEAD = C::KS0 < 6 ? C::KS0 : 6;
+        auto logits = [&](uint32_t nb, int db, auto DMA) -> v16f {
+            constexpr bool do_dma = decltype(DMA)::value;
+            uint32_t o[MAXK];
+            uint32_t dbuf = 0;
+            if constexpr (do_dma) {
+                dbuf = buf_of(db);
+#pragma unroll
+                for (int k = 0; k < MAXK; ++k) {
+                    const int I = w4 + C::NW * k;
+                    int r, col, base;
+                    piece_of<C>(I, lane, r, col, base);
+                    o[k] = (C::INSTRS % C::NW == 0 || I < C::INSTRS) ? lofs[db * kBlk + r] + col : 0u;
+                }
+            }
+            auto dma_k = [&](int k) {
+                const int I = w4 + C::NW * k;
+                if (C::INSTRS % C::NW == 0 || I < C::INSTRS) {
+                    int r, col, base;
+                    piece_of<C>(I, lane, r, col, base);
+                    dma16(kvb, o[k], dbuf + base);
+                }
+            };
+            uint32_t qa[C::TLQ], ra[C::RH];
 #pragma unroll
             for (int i = 0; i < C::TLQ; ++i) qa[i] = opaque(nb + qoff[i]);
 #pragma unroll
             for (int j = 0; j < C::RH; ++j) ra[j] = opaque(nb + roff[j]);
+            v4i av[C::KS0];
 #pragma unroll
             for (int i = 0; i < AHEAD; ++i) av[i] = qk_read(qa, ra, i);
-        }
-        const float mref = m_run == -INFINITY ? 0.f : m_run;
-        float pe[16], ls = 0.f;
-        v16f sacc = (v16f){};
-        __builtin_amdgcn_sched_barrier(0);
+            v16f sacc = (v16f){};
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < C::KS0; ++i) {
-            if constexpr (do_qk) {
+            for (int i = 0; i < C::KS0; ++i) {
                 if (i + AHEAD < C::KS0) av[i + AHEAD] = qk_read(qa, ra, i + AHEAD);
                 if (C::EVEN || i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
+                if constexpr (do_dma)
+                    if (i < MAXK) dma_k(i);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (do_exp)
-                if (i < 16) exp_elem(zc, i, mref, pe, ls);
-            if constexpr (do_dma)
-                if (i < MAXK) dma_k(i);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (do_exp) {
+            if constexpr (do_dma) {
 #pragma unroll
-            for (int e = C::KS0; e < 16; ++e) exp_elem(zc, e, mref, pe, ls);
+                for (int k = C::KS0; k < MAXK; ++k) dma_k(k);
+            }
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int r4 = 0; r4 < 4; ++r4)
+                lds_write16(sx_own + 1024 * r4,
+                            __builtin_bit_cast(v4i, (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2],
+                                                          sacc[4 * r4 + 3]}));
+            return sacc;
+        };
+        // Softmax of a block whose partials were exchanged: logits (own partial plus the other
+        // half's; addition commutes exactly, so both halves hold identical logits), masked
+        // rows, running max with lazy rescale (factor published for the value waves, 1 when
+        // the max did not move), then P^T of this wave's 16-row slice (u = dp) to `par`.
+        auto softmax = [&](const v16f& sacc, uint32_t vmask, int par) {
+            float z[16];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pf[u][e] = (__bf16)pe[8 * u + e];
-            l_run += ls;
-        }
-        if constexpr (do_dma) {
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const v4f b = __builtin_bit_cast(v4f, lds_read16(sx_other + 1024 * r4));
 #pragma unroll
-            for (int k = C::KS0; k < MAXK; ++k) dma_k(k);
-        }
-        return sacc;
-    };
+                for (int e = 0; e < 4; ++e) z[4 * r4 + e] = sacc[4 * r4 + e] + b[e];
+            }
+            if (vmask != 0xffffffffu) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
+                    if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
+                }
+            }
+            // med3(a, b, +inf) = max(a, b) for the non-NaN logits here; unlike fmaxf it needs
+            // no quieting of its inputs first
+            float mb = __builtin_amdgcn_fmed3f(z[0], z[1], INFINITY);
+#pragma unroll
+            for (int r = 2; r < 16; ++r) mb = __builtin_amdgcn_fmed3f(mb, z[r], INFINITY);
+            mb = __builtin_amdgcn_fmed3f(mb, __shfl_xor(mb, 32), INFINITY) * sm_log2;
+            float alpha = 1.f;
+            const bool bump = mb > m_run + kRescaleGap;
+            if (__ballot(bump) != 0ull) {
+                const bool fresh = m_run == -INFINITY;
+                const float m_new = bump ? mb : m_run;
+                alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);  // O is still 0 when fresh
+                m_run = m_new;
+                l_run *= alpha;
+            }
+            if (dp == 0 && half == 0) abuf[par][hg][mi] = alpha;
+            // p = 2^(sm_log2 * z - m_run); masked rows give exact zeros, also while no row has
+            // been seen (m_run = -inf is then replaced by 0)
+            const float mref = m_run == -INFINITY ? 0.f : m_run;
+            // the slice offset is a compile-time constant in each branch (a runtime index
+            // would put z in scratch memory)
+            auto exps = [&](auto OFF) {
+                v8bf pf;
+                float ls = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(z[decltype(OFF)::value + e], sm_log2, -mref));
+                    ls += pv;
+                    pf[e] = (__bf16)pv;
+                }
+                l_run += ls;
+                pbuf[par][hg][dp][lane] = __builtin_bit_cast(v4i, pf);
+            };
+            if (dp) exps(std::integral_constant<int, 8>{});
+            else exps(std::integral_constant<int, 0>{});
+        };
 
-    // Phase C: both halves of a head group publish their partial S^T.
-    auto phase_c = [&](const v16f& sacc) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            lds_write16(sx_own + 1024 * r4,
-                        __builtin_bit_cast(v4i, (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2],
-                                                      sacc[4 * r4 + 3]}));
-        lds_barrier();
-    };
+        if (nblk > 0) {
+            issue_block<C>(buf_of(0), kvb, lofs, w4, lane);
+            if (nblk > 1) issue_block<C>(buf_of(1), kvb, lofs + kBlk, w4, lane);
+            if (nblk > 1) wait_loads<C::LOADS_PER_WAVE>();
+            else wait_loads<0>();
+            land(0);
+            lds_barrier();                                   // block 0 visible
+            const v16f s0 = logits(buf_of(0), 0, std::false_type{});
+            lds_barrier();                                   // partials of block 0 exchanged
+            softmax(s0, lmask[0], 0);
+            for (int blk = 0; blk < nblk; ++blk) {
+                if (blk + 1 < nblk) {
+                    wait_loads<0>();
+                    land(blk + 1);
+                }
+                lds_barrier();                               // top of step blk
+                if (blk + 1 < nblk) {
+                    v16f sn;
+                    if (blk + 2 < nblk) sn = logits(buf_of(blk + 1), blk + 2, std::true_type{});
+                    else sn = logits(buf_of(blk + 1), 0, std::false_type{});
+                    lds_barrier();                           // partials exchanged
+                    softmax(sn, lmask[blk + 1], (blk + 1) & 1);
+                }
+            }
+        }
+        // row sums of this wave's rows (both lane halves) and the running max, for the
+        // value waves' normalisation
+        const float lh = l_run + __shfl_xor(l_run, 32);
+        if (half == 0) {
+            lfin[hg][dp][mi] = lh;
+            if (dp == 0) mfin[hg][mi] = m_run;
+        }
+        __syncthreads();
+        return;
+    }
 
-    // Phase D: O^T += V^T P^T for block `cb` (when PV), while the summed logits zn of the
-    // next block are read and reduced to their max (when NEXT).
-    auto phase_d = [&](uint32_t cb, const v8bf (&pf)[2], float (&zn)[16], uint32_t vmask_n, auto PV,
-                       auto NEXT) {
-        constexpr bool do_pv = decltype(PV)::value, do_next = decltype(NEXT)::value;
+    // ---------------- value product ----------------
+    v16f oacc[C::VT0];
+#pragma unroll
+    for (int vt = 0; vt < C::VT0; ++vt) oacc[vt] = (v16f){};
+    // value operand (tr16 read) of 16-row slice u, row quad h, tile t at
+    // voff[u][h][t % TLV] + 64*TLV*(t / TLV); tr16 source lane j of each 16-lane group points
+    // at block row 16u + 8*half + j/4 (+4 for h = 1) and value columns cl*8 + sub/2 .. +3
+    uint32_t voff[2][2][C::TLV];
+    {
+        const int vsub = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+        const int cl = vsub >> 3, sub = (vsub & 7) * 2;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int t = 0; t < C::TLV; ++t)
+                    voff[u][h][t] = RV::chunk(16 * u + 8 * half + (j16 >> 2) + 4 * h,
+                                              4 * (dp * C::VT0 + t) + cl) + sub;
+    }
+    auto vstep = [&](int blk, bool exch) {
+        const int par = blk & 1;
+        const v8bf p0 = __builtin_bit_cast(v8bf, pbuf[par][hg][0][lane]);
+        const v8bf p1 = __builtin_bit_cast(v8bf, pbuf[par][hg][1][lane]);
+        const float alpha = abuf[par][hg][mi];
+        if (__ballot(alpha != 1.f) != 0ull) {
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // MFMA results settle
+#pragma unroll
+            for (int vt = 0; vt < C::VT0; ++vt) scale_agpr(oacc[vt], alpha);
+            asm volatile("s_nop 4" ::: "memory");  // before the next MFMA reads them
+        }
+        const uint32_t cb = buf_of(blk);
         uint32_t va_[2][2][C::TLV];
-        v8bf va[2][C::VT0];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int t = 0; t < C::TLV; ++t) va_[u][h][t] = opaque(cb + voff[u][h][t]);
         auto vread = [&](int u, int t) {
             const uint32_t imm = 64 * C::TLV * (t / C::TLV);
             const v4s lo = ds_read_tr16(va_[u][0][t % C::TLV] + imm);
@@ -480,118 +509,35 @@ __global__ __launch_bounds__(256, 1) void sparse_mqa_kernel(
             const v2i l2 = __builtin_bit_cast(v2i, lo), h2 = __builtin_bit_cast(v2i, hi);
             return __builtin_bit_cast(v8bf, (v4i){l2.x, l2.y, h2.x, h2.y});
         };
-        if constexpr (do_pv) {
+        v8bf va[2][C::VT0];
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int t = 0; t < C::TLV; ++t) va_[u][h][t] = opaque(cb + voff[u][h][t]);
-#pragma unroll
-            for (int t = 0; t < C::VT0; ++t) va[0][t] = vread(0, t);
-        }
-        v4f a[4], b[4];
-        if constexpr (do_next) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                a[r4] = __builtin_bit_cast(v4f, lds_read16(sx0 + 1024 * r4));
-                b[r4] = __builtin_bit_cast(v4f, lds_read16(sx1 + 1024 * r4));
-            }
-        }
+        for (int t = 0; t < C::VT0; ++t) va[0][t] = vread(0, t);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (do_pv) {
-#pragma unroll
-            for (int t = 0; t < C::VT0; ++t) {
-                va[1][t] = vread(1, t);
-                oacc[t] = mfma_bf16(va[0][t], pf[0], oacc[t]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
 #pragma unroll
         for (int t = 0; t < C::VT0; ++t) {
-            if constexpr (do_pv) oacc[t] = mfma_bf16(va[1][t], pf[1], oacc[t]);
-            if constexpr (do_next) {
-#pragma unroll
-                for (int k = 0; k < 16 / C::VT0; ++k) {
-                    const int r = t * (16 / C::VT0) + k;
-                    zn[r] = a[r >> 2][r & 3] + b[r >> 2][r & 3];
-                    asm volatile("" : "+v"(zn[r]));
-                }
-            }
+            va[1][t] = vread(1, t);
+            oacc[t] = mfma_bf16(va[0][t], p0, oacc[t]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (do_next) {
+        if (exch) lds_barrier();  // the logit waves' partial exchange
 #pragma unroll
-            for (int r = C::VT0 * (16 / C::VT0); r < 16; ++r) zn[r] = a[r >> 2][r & 3] + b[r >> 2][r & 3];
-            rescale(block_max(zn, vmask_n));
-        }
+        for (int t = 0; t < C::VT0; ++t) oacc[t] = mfma_bf16(va[1][t], p1, oacc[t]);
 #pragma unroll
         for (int vt = 0; vt < C::VT0; ++vt) pin_agpr(oacc[vt]);
     };
-
-    // Software pipeline over the blocks (three LDS buffers).  Step b, with the logits of block
-    // b in zc and its max folded into m_run:
-    //   top  block b+1's loads have landed (own wait, then a barrier); block b-1's buffer is free
-    //   B    logit MFMAs of block b+1, with block b's exponentials and block b+2's direct loads
-    //   C    exchange of block b+1's partial logits
-    //   D    value MFMAs of block b, with block b+1's logits summed and reduced to their max.
-    // The steady state (b+2 < nblk) runs unrolled by two, the logits alternating between za and
-    // zb; the last steps take the general form.
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    auto top = [&](int blk) {
-        if (blk + 1 < nblk) {
-            wait_loads<0>();
-            land(blk + 1);
-        }
-        lds_barrier();
-    };
-    auto step_full = [&](int blk, float (&zc)[16], float (&zn)[16]) {
-        top(blk);
-        v8bf pf[2];
-        phase_c(phase_b(buf_of(blk + 1), zc, pf, blk + 2, T_{}, T_{}, T_{}));
-        phase_d(buf_of(blk), pf, zn, lmask[blk + 1], T_{}, T_{});
-    };
-    auto step_tail = [&](int blk, float (&zc)[16], float (&zn)[16]) {
-        top(blk);
-        v8bf pf[2];
-        if (blk + 2 < nblk) {
-            phase_c(phase_b(buf_of(blk + 1), zc, pf, blk + 2, T_{}, T_{}, T_{}));
-            phase_d(buf_of(blk), pf, zn, lmask[blk + 1], T_{}, T_{});
-        } else if (blk + 1 < nblk) {
-            phase_c(phase_b(buf_of(blk + 1), zc, pf, 0, T_{}, T_{}, F_{}));
-            phase_d(buf_of(blk), pf, zn, lmask[blk + 1], T_{}, T_{});
-        } else {
-            phase_b(0u, zc, pf, 0, F_{}, T_{}, F_{});
-            phase_d(buf_of(blk), pf, zn, 0u, T_{}, F_{});
-        }
-    };
-    if (nblk > 0) {  // the loop sits inside, so it is entered only after the prologue's waits
-        float za[16], zb[16];
-        v8bf pf0[2];
-        issue_block<C>(buf_of(0), kvb, lofs, wv, lane);
-        if (nblk > 1) issue_block<C>(buf_of(1), kvb, lofs + kBlk, wv, lane);
-        if (nblk > 1) wait_loads<C::LOADS_PER_WAVE>();
-        else wait_loads<0>();
-        land(0);
-        lds_barrier();
-        phase_c(phase_b(buf_of(0), za, pf0, 0, T_{}, F_{}, F_{}));
-        phase_d(0u, pf0, za, lmask[0], F_{}, T_{});
-        int blk = 0;
-        for (; blk + 3 < nblk; blk += 2) {
-            step_full(blk, za, zb);
-            step_full(blk + 1, zb, za);
-#pragma unroll
-            for (int i = 0; i < C::KS0; ++i) pin_agpr(qf[i]);
-        }
-        while (blk < nblk) {
-            step_tail(blk++, za, zb);
-            if (blk < nblk) step_tail(blk++, zb, za);
+    if (nblk > 0) {
+        lds_barrier();  // block 0 visible
+        lds_barrier();  // partials of block 0 exchanged
+        for (int blk = 0; blk < nblk; ++blk) {
+            lds_barrier();  // top of step blk: P^T of block blk visible
+            vstep(blk, blk + 1 < nblk);
         }
     }
+    __syncthreads();  // final row sums and max published
 
     // ---- epilogue ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = lfin[hg][0][mi] + lfin[hg][1][mi];
+    const float m_run = mfin[hg][mi];
     if (head >= H) return;
     if (!SPLIT) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
