@@ -197,11 +197,8 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t lds[3 * C::BUF];
     __shared__ uint32_t lofs[kMaxTopk];            // byte offset of each selected row (0 if empty)
     __shared__ uint32_t lmask[kMaxTopk / kBlk];    // per block: bit j = slot j holds a row
-    __shared__ __attribute__((aligned(16))) float sx[2][2][4][kWave][4];  // [group][half][r/4][lane][r%4]
-    __shared__ __attribute__((aligned(16))) v4i pbuf[2][2][2][kWave];     // P^T: [parity][group][slice][lane]
-    __shared__ float abuf[2][2][32];   // O rescale factor: [parity][group][head]
-    __shared__ float lfin[2][2][32];   // final row sums: [group][half][head]
-    __shared__ float mfin[2][32];      // final running max: [group][head]
+    // partial S^T tiles: [block parity][group][half][r/4][lane][r%4]
+    __shared__ __attribute__((aligned(16))) float sx[2][2][2][4][kWave][4];
 
     // Work item.  With two workgroups per row (64 heads each) the pair is issued 8 ids
     // apart, i.e. onto the same XCD, so the second gather of each latent row hits its L2.
@@ -259,24 +256,24 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
         return x;
     };
 
-    // Pipeline over the blocks (three LDS buffers for the gathered rows, two for P^T).  Step b:
-    //   top   block b+1's loads have landed (issuing waves wait, then a barrier); P^T of block b
-    //         and its rescale factor are visible; block b-1's buffer is free
-    //   logit waves:  logit MFMAs of block b+1 with block b+2's direct loads, exchange of the
-    //                 partial logits (barrier), softmax of block b+1 -> P^T, rescale factor
-    //   value waves:  rescale O if the max moved, value MFMAs of block b (half of them before
-    //                 the exchange barrier, half after)
-    // Both kinds of wave pass the same barriers in the same order; a logit wave and a value
-    // wave share each SIMD, so one's VALU work runs under the other's MFMAs.
+    // Pipeline over the blocks (three LDS buffers for the gathered rows, two for the partial
+    // logits), one barrier per step.  Step b:
+    //   logit waves:  partial logits of block b+1 over their half of the dims (direct loads of
+    //                 block b+2 between the MFMAs), published to LDS; then wait for block b+2
+    //   value waves:  logits of block b from both published partials, online softmax, and
+    //                 the value MFMAs of block b
+    //   barrier: block b+1's partials and block b+2's rows are visible; block b's buffer is free
+    // A logit wave and a value wave share each SIMD, so the softmax VALU work of one runs under
+    // the other's MFMAs.
     if (logit_wave) {
-        // ---------------- logits and softmax ----------------
+        // ---------------- partial logits ----------------
         // Logit k-slices of this wave's half: value slices dp*KSV2 + i (i < KSV2), then rope
         // slices KSV + dp*RH + j.  Lane l holds head 64*hh + 32*hg + l%32, dims 8*(l/32) .. +7
-        // of each slice.
+        // of each slice.  Loaded unconditionally from clamped addresses and masked afterwards,
+        // so all the loads fly together; then moved to AGPRs (MFMA B operands are read from
+        // there).
         const int nrope = min(C::RH, C::R - dp * C::RH);
         const int nks = C::KSV2 + nrope;
-        // Loaded unconditionally from clamped addresses and masked afterwards, so all the
-        // loads fly together; then moved to AGPRs (MFMA B operands are read from there).
         v8bf qf[C::KS0];
         {
             const uint16_t* qp = q + ((int64_t)ri.qrow * H + (head < H ? head : 0)) * DQK + 8 * half;
@@ -293,8 +290,6 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
                 pin_agpr(qf[i]);
             }
         }
-        float m_run = -INFINITY;  // running max of the base-2 logits of this lane's head
-        float l_run = 0.f;        // running sum over this wave's rows of this lane's head
         // Block row held by MFMA row i = l%32 of the logit product: lanes of each 32-lane half
         // must own 8 consecutive block rows per 16-row k-slice of the value product.
         const int srow = 16 * (mi >> 4) + 8 * ((mi >> 2) & 1) + 4 * ((mi >> 3) & 1) + (mi & 3);
@@ -305,8 +300,8 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
         for (int i = 0; i < C::TLQ; ++i) qoff[i] = RV::chunk(srow, dp * C::KSV + 2 * i + half);
 #pragma unroll
         for (int j = 0; j < C::RH; ++j) roff[j] = RV::BYTES + RR::chunk(srow, 2 * (dp * C::RH + j) + half);
-        const uint32_t sx_own = lds_addr(&sx[hg][dp][0][lane][0]);
-        const uint32_t sx_other = lds_addr(&sx[hg][1 - dp][0][lane][0]);
+        const uint32_t sx_own0 = lds_addr(&sx[0][hg][dp][0][lane][0]);
+        constexpr uint32_t SX_PAR = 2 * 2 * 4 * kWave * 4 * 4;  // bytes per parity
 
         auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
             const uint32_t vm = lmask[blk];
@@ -316,12 +311,13 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
             if (i < C::KSV2) return lds_read16(qa[i % C::TLQ] + 32 * C::TLQ * (i / C::TLQ));
             return lds_read16(ra[i - C::KSV2]);
         };
-        // Partial S^T of block `nb` over this wave's dims, published to the other half of the
-        // head group; the direct loads of block `db` (when DMA) go out between the MFMAs.
+        // Partial S^T of block `nb` over this wave's dims, published for the value waves; the
+        // direct loads of block `db` (when DMA) go out between the MFMAs.
         constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
         constexpr int AHEAD = C::KS0 < 6 ? C::KS0 : 6;
-        auto logits = [&](uint32_t nb, int db, auto DMA) -> v16f {
+        auto logits = [&](int nblk_idx, int db, auto DMA) {
             constexpr bool do_dma = decltype(DMA)::value;
+            const uint32_t nb = buf_of(nblk_idx);
             uint32_t o[MAXK];
             uint32_t dbuf = 0;
             if constexpr (do_dma) {
@@ -364,67 +360,12 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
 #pragma unroll
                 for (int k = C::KS0; k < MAXK; ++k) dma_k(k);
             }
+            const uint32_t so = sx_own0 + (uint32_t)(nblk_idx & 1) * SX_PAR;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4)
-                lds_write16(sx_own + 1024 * r4,
+                lds_write16(so + 1024 * r4,
                             __builtin_bit_cast(v4i, (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2],
                                                           sacc[4 * r4 + 3]}));
-            return sacc;
-        };
-        // Softmax of a block whose partials were exchanged: logits (own partial plus the other
-        // half's; addition commutes exactly, so both halves hold identical logits), masked
-        // rows, running max with lazy rescale (factor published for the value waves, 1 when
-        // the max did not move), then P^T of this wave's 16-row slice (u = dp) to `par`.
-        auto softmax = [&](const v16f& sacc, uint32_t vmask, int par) {
-            float z[16];
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const v4f b = __builtin_bit_cast(v4f, lds_read16(sx_other + 1024 * r4));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) z[4 * r4 + e] = sacc[4 * r4 + e] + b[e];
-            }
-            if (vmask != 0xffffffffu) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
-                    if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
-                }
-            }
-            // med3(a, b, +inf) = max(a, b) for the non-NaN logits here; unlike fmaxf it needs
-            // no quieting of its inputs first
-            float mb = __builtin_amdgcn_fmed3f(z[0], z[1], INFINITY);
-#pragma unroll
-            for (int r = 2; r < 16; ++r) mb = __builtin_amdgcn_fmed3f(mb, z[r], INFINITY);
-            mb = __builtin_amdgcn_fmed3f(mb, __shfl_xor(mb, 32), INFINITY) * sm_log2;
-            float alpha = 1.f;
-            const bool bump = mb > m_run + kRescaleGap;
-            if (__ballot(bump) != 0ull) {
-                const bool fresh = m_run == -INFINITY;
-                const float m_new = bump ? mb : m_run;
-                alpha = fresh ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);  // O is still 0 when fresh
-                m_run = m_new;
-                l_run *= alpha;
-            }
-            if (dp == 0 && half == 0) abuf[par][hg][mi] = alpha;
-            // p = 2^(sm_log2 * z - m_run); masked rows give exact zeros, also while no row has
-            // been seen (m_run = -inf is then replaced by 0)
-            const float mref = m_run == -INFINITY ? 0.f : m_run;
-            // the slice offset is a compile-time constant in each branch (a runtime index
-            // would put z in scratch memory)
-            auto exps = [&](auto OFF) {
-                v8bf pf;
-                float ls = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(z[decltype(OFF)::value + e], sm_log2, -mref));
-                    ls += pv;
-                    pf[e] = (__bf16)pv;
-                }
-                l_run += ls;
-                pbuf[par][hg][dp][lane] = __builtin_bit_cast(v4i, pf);
-            };
-            if (dp) exps(std::integral_constant<int, 8>{});
-            else exps(std::integral_constant<int, 0>{});
         };
 
         if (nblk > 0) {
@@ -433,40 +374,34 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
             if (nblk > 1) wait_loads<C::LOADS_PER_WAVE>();
             else wait_loads<0>();
             land(0);
-            lds_barrier();                                   // block 0 visible
-            const v16f s0 = logits(buf_of(0), 0, std::false_type{});
-            lds_barrier();                                   // partials of block 0 exchanged
-            softmax(s0, lmask[0], 0);
+            lds_barrier();  // block 0 visible
+            logits(0, 0, std::false_type{});
+            if (nblk > 1) {
+                wait_loads<0>();
+                land(1);
+            }
+            lds_barrier();  // block 0's partials and block 1's rows visible
             for (int blk = 0; blk < nblk; ++blk) {
                 if (blk + 1 < nblk) {
+                    if (blk + 2 < nblk) logits(blk + 1, blk + 2, std::true_type{});
+                    else logits(blk + 1, 0, std::false_type{});
+                }
+                if (blk + 2 < nblk) {
                     wait_loads<0>();
-                    land(blk + 1);
+                    land(blk + 2);
                 }
-                lds_barrier();                               // top of step blk
-                if (blk + 1 < nblk) {
-                    v16f sn;
-                    if (blk + 2 < nblk) sn = logits(buf_of(blk + 1), blk + 2, std::true_type{});
-                    else sn = logits(buf_of(blk + 1), 0, std::false_type{});
-                    lds_barrier();                           // partials exchanged
-                    softmax(sn, lmask[blk + 1], (blk + 1) & 1);
-                }
+                lds_barrier();  // end of step blk
             }
         }
-        // row sums of this wave's rows (both lane halves) and the running max, for the
-        // value waves' normalisation
-        const float lh = l_run + __shfl_xor(l_run, 32);
-        if (half == 0) {
-            lfin[hg][dp][mi] = lh;
-            if (dp == 0) mfin[hg][mi] = m_run;
-        }
-        __syncthreads();
         return;
     }
 
-    // ---------------- value product ----------------
+    // ---------------- softmax and value product ----------------
     v16f oacc[C::VT0];
 #pragma unroll
     for (int vt = 0; vt < C::VT0; ++vt) oacc[vt] = (v16f){};
+    float m_run = -INFINITY;  // running max of the base-2 logits of this lane's head
+    float l_run = 0.f;        // running sum over this lane's half of the block rows
     // value operand (tr16 read) of 16-row slice u, row quad h, tile t at
     // voff[u][h][t % TLV] + 64*TLV*(t / TLV); tr16 source lane j of each 16-lane group points
     // at block row 16u + 8*half + j/4 (+4 for h = 1) and value columns cl*8 + sub/2 .. +3
@@ -483,17 +418,71 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
                     voff[u][h][t] = RV::chunk(16 * u + 8 * half + (j16 >> 2) + 4 * h,
                                               4 * (dp * C::VT0 + t) + cl) + sub;
     }
-    auto vstep = [&](int blk, bool exch) {
-        const int par = blk & 1;
-        const v8bf p0 = __builtin_bit_cast(v8bf, pbuf[par][hg][0][lane]);
-        const v8bf p1 = __builtin_bit_cast(v8bf, pbuf[par][hg][1][lane]);
-        const float alpha = abuf[par][hg][mi];
-        if (__ballot(alpha != 1.f) != 0ull) {
-            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // MFMA results settle
+    const uint32_t sx0 = lds_addr(&sx[0][hg][0][0][lane][0]);
+    const uint32_t sx1 = lds_addr(&sx[0][hg][1][0][lane][0]);
+    constexpr uint32_t SX_PAR = 2 * 2 * 4 * kWave * 4 * 4;  // bytes per parity
+
+    // Logits of block blk from the two published partials (the same sum in the same order in
+    // both value waves of a group, so both hold identical softmax state), masked rows, running
+    // max with lazy rescale of O, then P^T as the two bf16 B operands (slices u = 0, 1).
+    auto softmax = [&](int blk, v8bf (&pf)[2]) {
+        const uint32_t po = (uint32_t)(blk & 1) * SX_PAR;
+        float z[16];
 #pragma unroll
-            for (int vt = 0; vt < C::VT0; ++vt) scale_agpr(oacc[vt], alpha);
-            asm volatile("s_nop 4" ::: "memory");  // before the next MFMA reads them
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const v4f a = __builtin_bit_cast(v4f, lds_read16(sx0 + po + 1024 * r4));
+            const v4f b = __builtin_bit_cast(v4f, lds_read16(sx1 + po + 1024 * r4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[4 * r4 + e] = a[e] + b[e];
         }
+        const uint32_t vmask = lmask[blk];
+        if (vmask != 0xffffffffu) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
+                if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
+            }
+        }
+        // max as a tree (med3(a, b, +inf) = max(a, b) for the non-NaN logits here; unlike
+        // fmaxf it needs no quieting of its inputs first), then across the lane halves with a
+        // lane swap instead of an LDS permute
+        auto mx = [](float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); };
+        float m8[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m8[r] = mx(z[2 * r], z[2 * r + 1]);
+        float mb = mx(mx(mx(m8[0], m8[1]), mx(m8[2], m8[3])), mx(mx(m8[4], m8[5]), mx(m8[6], m8[7])));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
+        mb = mx(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sm_log2;
+        const bool bump = mb > m_run + kRescaleGap;
+        if (__ballot(bump) != 0ull) {
+            const bool fresh = m_run == -INFINITY;
+            const float m_new = bump ? mb : m_run;
+            const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            if (__ballot(!fresh) != 0ull) {
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // MFMA results settle
+#pragma unroll
+                for (int vt = 0; vt < C::VT0; ++vt) scale_agpr(oacc[vt], alpha);
+                asm volatile("s_nop 4" ::: "memory");  // before the next MFMA reads them
+            }
+        }
+        // p = 2^(sm_log2 * z - m_run); masked rows give exact zeros, also while no row has been
+        // seen (m_run = -inf is then replaced by 0)
+        const float mref = m_run == -INFINITY ? 0.f : m_run;
+        float ls = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(z[8 * u + e], sm_log2, -mref));
+                ls += pv;
+                pf[u][e] = (__bf16)pv;
+            }
+        l_run += ls;
+    };
+    // O^T += V^T P^T over this wave's value tiles.
+    auto values = [&](int blk, const v8bf (&pf)[2]) {
         const uint32_t cb = buf_of(blk);
         uint32_t va_[2][2][C::TLV];
 #pragma unroll
@@ -516,28 +505,27 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
 #pragma unroll
         for (int t = 0; t < C::VT0; ++t) {
             va[1][t] = vread(1, t);
-            oacc[t] = mfma_bf16(va[0][t], p0, oacc[t]);
+            oacc[t] = mfma_bf16(va[0][t], pf[0], oacc[t]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (exch) lds_barrier();  // the logit waves' partial exchange
 #pragma unroll
-        for (int t = 0; t < C::VT0; ++t) oacc[t] = mfma_bf16(va[1][t], p1, oacc[t]);
+        for (int t = 0; t < C::VT0; ++t) oacc[t] = mfma_bf16(va[1][t], pf[1], oacc[t]);
 #pragma unroll
         for (int vt = 0; vt < C::VT0; ++vt) pin_agpr(oacc[vt]);
     };
     if (nblk > 0) {
         lds_barrier();  // block 0 visible
-        lds_barrier();  // partials of block 0 exchanged
+        lds_barrier();  // block 0's partials and block 1's rows visible
         for (int blk = 0; blk < nblk; ++blk) {
-            lds_barrier();  // top of step blk: P^T of block blk visible
-            vstep(blk, blk + 1 < nblk);
+            v8bf pf[2];
+            softmax(blk, pf);
+            values(blk, pf);
+            lds_barrier();  // end of step blk
         }
     }
-    __syncthreads();  // final row sums and max published
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
 
     // ---- epilogue ----
-    const float l_tot = lfin[hg][0][mi] + lfin[hg][1][mi];
-    const float m_run = mfin[hg][mi];
     if (head >= H) return;
     if (!SPLIT) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
