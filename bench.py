@@ -17,6 +17,7 @@ Besides the end-to-end rate the line carries:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -36,6 +37,39 @@ METRIC = "DSA prefill tokens/s at 128K (+ indexer FP8 TFLOP/s); decode µs/token
 PEAK = {"fp8": 5000.0, "bf16": 2500.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s (MI355X)
 FLOP_INDEXER_PAIR = 2 * 64 * 128       # per causal (query, key) pair
 FLOP_MQA_PAIR = 2 * 128 * (576 + 512)  # per selected (query, key) pair
+
+
+# HBM traffic per launch of a kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+# profiles/traffic.json together with a hash of the kernel's sources; reported only while the
+# sources are unchanged.
+KERNEL_SOURCES = {
+    "sparse_mqa_kernel": ["sparse_attention_long_lightning_amd/csrc/mqa.hip",
+                          "sparse_attention_long_lightning_amd/csrc/common.hpp"],
+    "indexer_prefill_kernel": ["sparse_attention_long_lightning_amd/csrc/indexer.hip",
+                               "sparse_attention_long_lightning_amd/csrc/common.hpp"],
+    "topk_kernel": ["sparse_attention_long_lightning_amd/csrc/topk.hip",
+                    "sparse_attention_long_lightning_amd/csrc/common.hpp"],
+}
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch (fetched + written) if recorded for the current sources, else None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+            rec = json.load(fh).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_hash(kernel):
+        return None
+    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
 def log(msg):
@@ -166,7 +200,7 @@ def decode_case(dev, steps):
                 mean_context=round(nkeys / B), hbm_floor_mb=round((nkeys * 132 + B * 2048 * 1152) / 1e6, 1))
 
 
-def cpu_baseline(c, budget_s=20.0, max_rows=64):
+def cpu_baseline(c, budget_s=20.0, max_rows=192):
     """The oracle on uniformly spaced query rows of the same prefill (indexer over every
     earlier key, top-k, MQA).  Rows are processed in growing batches until ~budget_s."""
     import oracle
@@ -209,12 +243,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first copy BYTES between two device buffers (a plain copy of known size "
+                         "that calibrates the HBM byte counters of a profiled run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_calibration} bytes done")
+        del src, dst
     L = args.seq_len
     c = prefill_case(L, dev)
     log(f"workspace {c['ws'].numel() / 2**30:.2f} GiB")
@@ -272,7 +316,7 @@ def main():
             roof = dict(kernel="topk_kernel", bound="hbm", achieved=round(per / avg, 1),
                         peak=PEAK["hbm"], unit="GB/s")
         roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-        roof["traffic"] = None
+        roof["traffic"] = recorded_traffic(roof["kernel"])
         roof["avg_launch_ms"] = round(avg * 1e3, 3)
         line["roofline"] = roof
         log(f"stages {json.dumps(stages)}")
