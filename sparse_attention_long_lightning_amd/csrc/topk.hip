@@ -30,6 +30,7 @@ constexpr int kBins1 = 2048;  // key bits 31..21
 constexpr int kBins2 = 2048;  // key bits 20..10
 constexpr int kBins3 = 1024;  // key bits 9..0
 constexpr int kCap = 8192;    // list entries held in LDS
+constexpr int kUnroll = 4;    // 256-element pieces per wave and loop iteration
 
 struct Smem {
     union {
@@ -142,13 +143,18 @@ __global__ __launch_bounds__(kThreads, 2) void topk_kernel(const float* __restri
     for (int j = tid; j < kWaves * kBins1; j += kThreads) (&sm.u.hist_w[0][0])[j] = 0u;
     __syncthreads();
     uint32_t* hw = sm.u.hist_w[wv];
-    for (int e0 = sb; e0 < se; e0 += 256) {
-        uint32_t k[4];
-        bool ok[4];
-        load4(x, e0 + 4 * lane, se, k, ok);
+    // kUnroll pieces per lane are loaded before any is used, so each wave keeps kUnroll KiB
+    // in flight (the row streams from HBM at the memory latency otherwise)
+    for (int e0 = sb; e0 < se; e0 += 256 * kUnroll) {
+        uint32_t k[kUnroll][4];
+        bool ok[kUnroll][4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (ok[c]) atomicAdd(&hw[k[c] >> 21], 1u);
+        for (int u = 0; u < kUnroll; ++u) load4(x, e0 + 256 * u + 4 * lane, se, k[u], ok[u]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (ok[u][c]) atomicAdd(&hw[k[u][c] >> 21], 1u);
     }
     __syncthreads();
     for (int b = tid; b < kBins1; b += kThreads) {
@@ -175,31 +181,37 @@ __global__ __launch_bounds__(kThreads, 2) void topk_kernel(const float* __restri
         // ---- pass 2: compact everything at or above b1, in position order ----
         int run = 0;
         for (int w = 0; w < wv; ++w) run += sm.wcnt[w];
-        for (int e0 = sb; e0 < se; e0 += 256) {
-            uint32_t k[4];
-            bool ok[4];
-            const int e = e0 + 4 * lane;
-            load4(x, e, se, k, ok);
-            int f = 0;
-            bool q[4];
+        for (int e00 = sb; e00 < se; e00 += 256 * kUnroll) {
+            uint32_t kk4[kUnroll][4];
+            bool ok4[kUnroll][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                q[c] = ok[c] && (int)(k[c] >> 21) >= b1;
-                f += q[c];
-            }
-            if (__ballot(f > 0) == 0ull) continue;
-            int total;
-            int j = run + wave_slot(f, total);
+            for (int u = 0; u < kUnroll; ++u) load4(x, e00 + 256 * u + 4 * lane, se, kk4[u], ok4[u]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (q[c]) {
-                    if (j < kCap) {
-                        sm.u.cand.key[j] = k[c];
-                        sm.u.cand.pos[j] = e + c;
-                    }
-                    ++j;
+            for (int u = 0; u < kUnroll; ++u) {  // pieces in position order
+                const uint32_t* k = kk4[u];
+                const bool* ok = ok4[u];
+                const int e = e00 + 256 * u + 4 * lane;
+                int f = 0;
+                bool q[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    q[c] = ok[c] && (int)(k[c] >> 21) >= b1;
+                    f += q[c];
                 }
-            run += total;
+                if (__ballot(f > 0) == 0ull) continue;
+                int total;
+                int j = run + wave_slot(f, total);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (q[c]) {
+                        if (j < kCap) {
+                            sm.u.cand.key[j] = k[c];
+                            sm.u.cand.pos[j] = e + c;
+                        }
+                        ++j;
+                    }
+                run += total;
+            }
         }
         for (int b = tid; b < kBins2; b += kThreads) sm.hist[b] = 0u;
         __syncthreads();
