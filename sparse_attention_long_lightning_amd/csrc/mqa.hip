@@ -57,33 +57,43 @@ struct Region {
 
 template <int H, int DQK, int DV>
 struct MqaCfg {
-    static constexpr int THREADS = 512;        // 4 logit waves + 4 value waves (2 groups x 2 halves)
-    static constexpr int NW = 4;
+    // 8 waves in three roles; wave w shares its SIMD with wave w + 4.
+    //   waves 0, 1        logits over the first half of the dims for head group 0 / 1
+    //                     (32 heads each), then the online softmax of the group
+    //   waves 4, 5        logits over the second half of the dims of the same group,
+    //                     handed to wave w - 4 through LDS, and the direct global->LDS loads
+    //                     of the gathered rows
+    //   waves 2, 3, 6, 7  value product (64 heads x a quarter of the DV dims each)
+    // Splitting each group's logits over two waves of one SIMD halves the LDS operand bytes
+    // each wave must read per block (a single wave's LDS read rate is the limit otherwise).
+    static constexpr int THREADS = 512;
+    static constexpr int NDW = 2;              // waves issuing direct loads
+    static constexpr int NBUF = 4;             // gathered blocks resident in LDS
+    static constexpr int RING = 4;             // blocks of row offsets staged in LDS
     static constexpr int NHH = (H + 63) / 64;  // workgroups per query row, 64 heads each
     static constexpr int KS = DQK / 16;        // k-slices of the logit product
+    static constexpr int KH = (KS + 1) / 2;    // slices of the first half (waves 0, 1)
     static constexpr int KSV = DV / 16;        // k-slices that fall in the value region
-    static constexpr int KSV2 = KSV / 2;       // value slices per half
-    static constexpr int R = KS - KSV;         // rope slices
-    static constexpr int RH = (R + 1) / 2;     // rope slices of half 0 (half 1 takes the rest)
-    static constexpr int KS0 = KSV2 + RH;      // slices of half 0 (the larger half)
     static constexpr int VT = DV / 32;         // 32-wide value tiles
-    static constexpr int VT0 = VT / 2;         // value tiles per half
+    static constexpr int NVW = VT < 4 ? VT : 4;  // value waves with product work
+    static constexpr int VTW = VT / NVW;         // value tiles per value wave
     using RV = Region<DV * 2 / 16>;
     using RR = Region<(DQK - DV) * 2 / 16>;
     static constexpr int BUF = RV::BYTES + RR::BYTES;
     static constexpr int INSTRS = RV::INSTRS + RR::INSTRS;
-    static constexpr int ROW_BYTES = DQK * 2;           // bytes of one latent row in memory
-    static constexpr int VBYTES = DV * 2;               // bytes of its value part
-    static constexpr int LOADS_PER_WAVE = INSTRS / NW;  // direct loads per wave and block (min)
-    static constexpr bool EVEN = R % 2 == 0;            // both halves have KS0 slices
-    static constexpr int QK_AHEAD = KS0 < 9 ? KS0 : 9;  // logit operand loads kept in flight
+    static constexpr int ROW_BYTES = DQK * 2;              // bytes of one latent row in memory
+    static constexpr int VBYTES = DV * 2;                  // bytes of its value part
+    static constexpr int MAXK = (INSTRS + NDW - 1) / NDW;  // direct loads per loading wave and block
+    static constexpr int LOADS_PER_WAVE = INSTRS / NDW;    // fewest of a loading wave per block
+    static constexpr int QK_AHEAD = KH < 6 ? KH : 6;       // logit operand reads kept in flight
     // Per-lane LDS offsets are kept for TLQ logit slices and TLV value tiles only: the rest
     // differ by a multiple of the swizzle period and reach the reads as immediate offsets.
     static constexpr int W = RV::SWZ_BITS;
-    static constexpr int TLQ = (KSV % (1 << W) == 0 && KSV2 % (1 << (W - 1)) == 0) ? (1 << (W - 1)) : KSV2;
-    static constexpr int TLV = ((4 * VT0) % (1 << W) == 0 && VT0 % (1 << (W - 2)) == 0) ? (1 << (W - 2)) : VT0;
-    static_assert(DQK % 16 == 0 && DV % 64 == 0, "unsupported latent widths");
+    static constexpr int TLQ = KSV % (1 << (W - 1)) == 0 ? (1 << (W - 1)) : KSV;
+    static constexpr int TLV = ((4 * VTW) % (1 << W) == 0 && VTW % (1 << (W - 2)) == 0) ? (1 << (W - 2)) : VTW;
+    static_assert(DQK % 16 == 0 && DV % 64 == 0 && VT % NVW == 0, "unsupported latent widths");
     static_assert(NHH <= 2, "at most 128 heads");
+    static_assert(3 * MAXK <= 63, "direct loads of three blocks must fit the load counter");
 };
 
 __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
@@ -96,6 +106,23 @@ __device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); 
 
 // Keeps a query fragment (an MFMA B operand, read as is from AGPRs) out of the VGPRs.
 __device__ __forceinline__ void pin_agpr(v8bf& x) { asm volatile("" : "+a"(x)); }
+__device__ __forceinline__ void pin_vgpr(v8bf& x) { asm volatile("" : "+v"(x)); }
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// max(a, b, c) for non-NaN inputs, as one instruction.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 
 // x *= alpha on a tile held in AGPRs, element by element through one VGPR (VALU instructions
 // cannot read AGPRs), so the tile never has to live in VGPRs.
@@ -140,26 +167,24 @@ __device__ __forceinline__ void piece_of(int I, int lane, int& r, int& col, int&
 
 // Issues the direct global->LDS loads of one block of kBlk latent rows into the buffer at
 // LDS address `buf`; `offs` points at the block's kBlk row byte offsets in LDS (empty slots
-// hold 0, i.e. row 0 of the sequence, and are zeroed by zero_empty_rows once landed).  The
-// wave's instruction slots are fixed at compile time (I = wv + NW*k), so the sequence is
-// fully unrolled: all offset reads first, then the loads.  Every wave issues the same number
-// of instructions for every block, so the wait can count them.
+// hold 0, i.e. row 0 of the sequence, and are zeroed by zero_empty_rows once landed).  Load
+// wave dw owns instructions I = dw + NDW*k, fixed at compile time, so the sequence is fully
+// unrolled: all offset reads first, then the loads.
 template <class C>
 __device__ __forceinline__ void issue_block(uint32_t buf, const uint8_t* kvb, const uint32_t* offs,
-                                            int wv, int lane) {
-    constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
-    constexpr bool FULL = C::INSTRS % C::NW == 0;  // every wave has MAXK slots
-    uint32_t o[MAXK];
+                                            int dw, int lane) {
+    constexpr bool FULL = C::INSTRS % C::NDW == 0;  // every load wave has MAXK slots
+    uint32_t o[C::MAXK];
 #pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-        const int I = wv + C::NW * k;
+    for (int k = 0; k < C::MAXK; ++k) {
+        const int I = dw + C::NDW * k;
         int r, col, base;
         piece_of<C>(I, lane, r, col, base);
         o[k] = (FULL || I < C::INSTRS) ? offs[r] + col : 0u;
     }
 #pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-        const int I = wv + C::NW * k;
+    for (int k = 0; k < C::MAXK; ++k) {
+        const int I = dw + C::NDW * k;
         if (FULL || I < C::INSTRS) {
             int r, col, base;
             piece_of<C>(I, lane, r, col, base);
@@ -168,15 +193,14 @@ __device__ __forceinline__ void issue_block(uint32_t buf, const uint8_t* kvb, co
     }
 }
 
-// Zeroes the pieces of empty rows that this wave loaded itself (so the direct load has
+// Zeroes the pieces of empty rows that this load wave moved itself (so the direct load has
 // landed before the store, in this wave's program order).  Empty rows then contribute exact
-// zeros to both products.
+// zeros to both products whatever row 0 of the sequence holds.
 template <class C>
-__device__ __forceinline__ void zero_empty_rows(uint32_t buf, uint32_t vmask, int wv, int lane) {
-    constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
+__device__ __forceinline__ void zero_empty_rows(uint32_t buf, uint32_t vmask, int dw, int lane) {
 #pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-        const int I = wv + C::NW * k;
+    for (int k = 0; k < C::MAXK; ++k) {
+        const int I = dw + C::NDW * k;
         if (I < C::INSTRS) {
             int r, col, base;
             piece_of<C>(I, lane, r, col, base);
@@ -185,6 +209,14 @@ __device__ __forceinline__ void zero_empty_rows(uint32_t buf, uint32_t vmask, in
     }
 }
 
+// Waits until at most N direct loads of this wave are outstanding, N chosen at run time
+// among the counts the pipeline uses.
+template <class C>
+__device__ __forceinline__ void wait_blocks_left(int nb) {
+    if (nb >= 2) wait_loads<2 * C::LOADS_PER_WAVE>();
+    else if (nb == 1) wait_loads<C::LOADS_PER_WAVE>();
+    else wait_loads<0>();
+}
 
 template <int H, int DQK, int DV, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
@@ -194,11 +226,15 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     using C = MqaCfg<H, DQK, DV>;
     using RV = typename C::RV;
     using RR = typename C::RR;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[3 * C::BUF];
-    __shared__ uint32_t lofs[kMaxTopk];            // byte offset of each selected row (0 if empty)
-    __shared__ uint32_t lmask[kMaxTopk / kBlk];    // per block: bit j = slot j holds a row
-    // partial S^T tiles: [block parity][group][half][r/4][lane][r%4]
-    __shared__ __attribute__((aligned(16))) float sx[2][2][2][4][kWave][4];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[C::NBUF * C::BUF];
+    // P^T operands of the value product: [head group][16-row slice][lane] x 8 bf16
+    __shared__ __attribute__((aligned(16))) v4i pl[2][2][kWave];
+    // second-half logit tiles handed from waves 4, 5 to waves 0, 1: [group][r/4][lane][r%4]
+    __shared__ __attribute__((aligned(16))) v4f sx[2][4][kWave];
+    __shared__ float al[2][32];                // per-head rescale factor of O for the block
+    __shared__ uint32_t rofs[C::RING][kBlk];   // row byte offsets of staged blocks
+    __shared__ uint32_t rmask[C::RING];        // per staged block: bit j = slot j holds a row
+    __shared__ float fin_l[2][32];             // softmax denominators at the end
 
     // Work item.  With two workgroups per row (64 heads each) the pair is issued 8 ids
     // apart, i.e. onto the same XCD, so the second gather of each latent row hits its L2.
@@ -215,10 +251,6 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     const int split = SPLIT ? blockIdx.y : 0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
-    const bool logit_wave = wv < 4;  // waves 0-3: logits and softmax; 4-7: value product
-    const int w4 = wv & 3;
-    const int hg = w4 & 1;  // head group: 32 heads
-    const int dp = w4 >> 1;  // half: of the logit dims (logit waves) or value tiles (value waves)
     const RowInfo ri = row_info(map, row);
     const int per = SPLIT ? (((topk + n_split - 1) / n_split + kBlk - 1) / kBlk) * kBlk : topk;
     const int j0 = split * per;
@@ -226,28 +258,31 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     const int nblk = j1 > j0 ? (j1 - j0 + kBlk - 1) / kBlk : 0;
     const int32_t* irow = idx + (int64_t)row * topk;
     const uint8_t* kvb = (const uint8_t*)(kv + (int64_t)ri.kbase * DQK);
-    const int head = hh * 64 + hg * 32 + (lane & 31);
     const int half = lane >> 5;
     const int mi = lane & 31;
     const int j16 = lane & 15;
     const uint32_t lds0 = lds_addr(lds);
 
-    // Selected rows of the work item, staged in LDS once: byte offsets (row 0 for an empty
-    // slot) and per-block occupancy masks.  A row's offset must fit in 31 bits.
-    for (int j = tid; j < nblk * kBlk; j += C::THREADS) {
-        const int id = j0 + j < j1 ? irow[j0 + j] : -1;
-        lofs[j] = id >= 0 ? (uint32_t)id * (uint32_t)C::ROW_BYTES : 0u;
+    // Row offsets (row 0 for an empty slot; a row's offset must fit in 31 bits) and occupancy
+    // of block b, staged in ring slot b % RING: the first RING blocks here, the rest by wave 0
+    // one step before the loads need them.
+    auto stage = [&](int b, int id) {  // lanes 0..31 hold the ids of the block's slots
+        if (lane < kBlk) rofs[b % C::RING][lane] = id >= 0 ? (uint32_t)id * (uint32_t)C::ROW_BYTES : 0u;
         const uint64_t m = __ballot(id >= 0);
-        if (lane == 0) lmask[j >> 5] = (uint32_t)m;
-        if (lane == 32) lmask[j >> 5] = (uint32_t)(m >> 32);
-    }
+        if (lane == 0) rmask[b % C::RING] = (uint32_t)m;
+    };
+    auto load_ids = [&](int b) {
+        const int j = j0 + b * kBlk + lane;
+        return (lane < kBlk && j < j1) ? irow[j] : -1;
+    };
+    if (wv < C::RING && wv < nblk) stage(wv, load_ids(wv));
     __syncthreads();
 
     // LDS address of block blk's buffer.  Passed through readfirstlane so that it stays one
     // opaque scalar per step: otherwise the compiler strength-reduces it into per-lane
     // induction variables and loses the immediate offsets of the reads.
     auto buf_of = [&](int blk) {
-        return (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(blk % 3) * C::BUF);
+        return (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(blk % C::NBUF) * C::BUF);
     };
     // Per-lane addresses base + off, made opaque so that constant parts added afterwards go
     // into the instructions' offset field instead of into one add per read.
@@ -256,306 +291,348 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
         return x;
     };
 
-    // Pipeline over the blocks (three LDS buffers for the gathered rows, two for the partial
-    // logits), one barrier per step.  Step b:
-    //   logit waves:  partial logits of block b+1 over their half of the dims (direct loads of
-    //                 block b+2 between the MFMAs), published to LDS; then wait for block b+2
-    //   value waves:  logits of block b from both published partials, online softmax, and
-    //                 the value MFMAs of block b
-    //   barrier: block b+1's partials and block b+2's rows are visible; block b's buffer is free
-    // A logit wave and a value wave share each SIMD, so the softmax VALU work of one runs under
-    // the other's MFMAs.
-    if (logit_wave) {
-        // ---------------- partial logits ----------------
-        // Logit k-slices of this wave's half: value slices dp*KSV2 + i (i < KSV2), then rope
-        // slices KSV + dp*RH + j.  Lane l holds head 64*hh + 32*hg + l%32, dims 8*(l/32) .. +7
-        // of each slice.  Loaded unconditionally from clamped addresses and masked afterwards,
-        // so all the loads fly together; then moved to AGPRs (MFMA B operands are read from
-        // there).
-        const int nrope = min(C::RH, C::R - dp * C::RH);
-        const int nks = C::KSV2 + nrope;
-        v8bf qf[C::KS0];
+    // Pipeline over the blocks: a prologue step (-1) and steps 0 .. nblk-1, each with a
+    // mid-step and an end barrier.  Step b:
+    //   waves 0, 1:   first half of block b+1's logits; after the mid-step barrier, add the
+    //                 second half, run the online softmax and publish block b+1's P^T and
+    //                 rescale factors
+    //   waves 4, 5:   hand over the second half of block b+1 (computed in step b-1); issue
+    //                 the direct loads of block b+3 into the buffer block b-1 used and wait
+    //                 for block b+2; after the mid-step barrier, the second half of block
+    //                 b+2, so that these MFMAs run beside the softmax of waves 0, 1 on the
+    //                 same SIMD
+    //   value waves:  read block b's P^T (published in step b-1); rescale O if needed and
+    //                 O^T += V^T P^T for block b, half on each side of the mid-step barrier
+    //   end barrier:  block b+1's P^T is visible; block b's buffer is free
+    if (wv != 2 && wv != 3 && wv != 6 && wv != 7) {
+        // ---------------- logits (and softmax on waves 0, 1) ----------------
+        const bool main = wv < 2;
+        const int hg = wv & 1;
+        const int head = hh * 64 + hg * 32 + mi;
+        const int i0 = main ? 0 : C::KH;              // first logit slice of this wave
+        const int nks = main ? C::KH : C::KS - C::KH;  // slices of this wave
+        // Query fragments: lane l holds head 64*hh + 32*hg + l%32, dims 16 i + 8*(l/32) .. +7
+        // of slice i = i0 + j.  Loaded unconditionally from clamped addresses and masked
+        // afterwards, so all the loads fly together; then kept in AGPRs (MFMA B operands are
+        // read from there).
+        v8bf qf[C::KH];
         {
             const uint16_t* qp = q + ((int64_t)ri.qrow * H + (head < H ? head : 0)) * DQK + 8 * half;
-            v4i v[C::KS0];
+            v4i v[C::KH];
 #pragma unroll
-            for (int i = 0; i < C::KS0; ++i) {
-                const int ks = i < C::KSV2 ? dp * C::KSV2 + i : C::KSV + dp * C::RH + (i - C::KSV2);
-                v[i] = *(const v4i*)(qp + 16 * min(ks, C::KS - 1));
-            }
+            for (int j = 0; j < C::KH; ++j) v[j] = *(const v4i*)(qp + 16 * min(i0 + j, C::KS - 1));
 #pragma unroll
-            for (int i = 0; i < C::KS0; ++i) {
-                const bool ok = head < H && i < nks;
-                qf[i] = __builtin_bit_cast(v8bf, ok ? v[i] : (v4i){0, 0, 0, 0});
-                pin_agpr(qf[i]);
+            for (int j = 0; j < C::KH; ++j) {
+                qf[j] = __builtin_bit_cast(v8bf, head < H && j < nks ? v[j] : (v4i){0, 0, 0, 0});
+                pin_agpr(qf[j]);
             }
         }
         // Block row held by MFMA row i = l%32 of the logit product: lanes of each 32-lane half
         // must own 8 consecutive block rows per 16-row k-slice of the value product.
         const int srow = 16 * (mi >> 4) + 8 * ((mi >> 2) & 1) + 4 * ((mi >> 3) & 1) + (mi & 3);
-        // Per-lane LDS offsets within a block buffer: logit operand of value slice i at
-        // qoff[i % TLQ] + 32*TLQ*(i / TLQ), of rope slice j at roff[j].
-        uint32_t qoff[C::TLQ], roff[C::RH];
-#pragma unroll
-        for (int i = 0; i < C::TLQ; ++i) qoff[i] = RV::chunk(srow, dp * C::KSV + 2 * i + half);
-#pragma unroll
-        for (int j = 0; j < C::RH; ++j) roff[j] = RV::BYTES + RR::chunk(srow, 2 * (dp * C::RH + j) + half);
-        const uint32_t sx_own0 = lds_addr(&sx[0][hg][dp][0][lane][0]);
-        constexpr uint32_t SX_PAR = 2 * 2 * 4 * kWave * 4 * 4;  // bytes per parity
-
-        auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
-            const uint32_t vm = lmask[blk];
-            if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, w4, lane);
-        };
-        auto qk_read = [&](const uint32_t (&qa)[C::TLQ], const uint32_t (&ra)[C::RH], int i) {
-            if (i < C::KSV2) return lds_read16(qa[i % C::TLQ] + 32 * C::TLQ * (i / C::TLQ));
-            return lds_read16(ra[i - C::KSV2]);
-        };
-        // Partial S^T of block `nb` over this wave's dims, published for the value waves; the
-        // direct loads of block `db` (when DMA) go out between the MFMAs.
-        constexpr int MAXK = (C::INSTRS + C::NW - 1) / C::NW;
-        constexpr int AHEAD = C::KS0 < 6 ? C::KS0 : 6;
-        auto logits = [&](int nblk_idx, int db, auto DMA) {
-            constexpr bool do_dma = decltype(DMA)::value;
-            const uint32_t nb = buf_of(nblk_idx);
-            uint32_t o[MAXK];
-            uint32_t dbuf = 0;
-            if constexpr (do_dma) {
-                dbuf = buf_of(db);
-#pragma unroll
-                for (int k = 0; k < MAXK; ++k) {
-                    const int I = w4 + C::NW * k;
-                    int r, col, base;
-                    piece_of<C>(I, lane, r, col, base);
-                    o[k] = (C::INSTRS % C::NW == 0 || I < C::INSTRS) ? lofs[db * kBlk + r] + col : 0u;
-                }
+        // LDS offsets of the logit operands within a block buffer, rebuilt for every read from
+        // two lane constants per region (fewer live registers): value slice i sits at chunk
+        // (2i + half) ^ swz(srow) = 2i ^ (half ^ swz(srow)) of row srow, plus 32*TLQ*(i / TLQ)
+        // bytes for the slices past the swizzle period; rope slice j likewise in the rope region.
+        const uint32_t qrow = srow * RV::PITCH, qx16 = 16 * (half ^ RV::swz(srow));
+        const uint32_t rrow = RV::BYTES + srow * RR::PITCH, rx16 = 16 * (half ^ RR::swz(srow));
+        auto qk_read = [&](uint32_t qb, uint32_t rb, int i) {
+            if (i < C::KSV) {
+                const int ii = i % C::TLQ;
+                return lds_read16(((uint32_t)(32 * ii) ^ qx16) + qb + 32 * C::TLQ * (i / C::TLQ));
             }
-            auto dma_k = [&](int k) {
-                const int I = w4 + C::NW * k;
-                if (C::INSTRS % C::NW == 0 || I < C::INSTRS) {
-                    int r, col, base;
-                    piece_of<C>(I, lane, r, col, base);
-                    dma16(kvb, o[k], dbuf + base);
-                }
-            };
-            uint32_t qa[C::TLQ], ra[C::RH];
+            return lds_read16(((uint32_t)(32 * (i - C::KSV)) ^ rx16) + rb);
+        };
+        // This wave's half of the logit tile S^T of block blk (fp32, 16 values per lane).
+        // The slice index is compile-time per wave kind, so the two kinds get separate code.
+        auto half_logits = [&](int blk, auto MAIN) {
+            constexpr bool M = decltype(MAIN)::value;
+            constexpr int I0 = M ? 0 : C::KH;
+            constexpr int N = M ? C::KH : C::KS - C::KH;
+            constexpr int AH = C::QK_AHEAD < N ? C::QK_AHEAD : N;
+            const uint32_t nb = buf_of(blk);
+            const uint32_t qb = opaque(nb + qrow), rb = opaque(nb + rrow);
+            v4i av[C::KH];
 #pragma unroll
-            for (int i = 0; i < C::TLQ; ++i) qa[i] = opaque(nb + qoff[i]);
-#pragma unroll
-            for (int j = 0; j < C::RH; ++j) ra[j] = opaque(nb + roff[j]);
-            v4i av[C::KS0];
-#pragma unroll
-            for (int i = 0; i < AHEAD; ++i) av[i] = qk_read(qa, ra, i);
+            for (int j = 0; j < AH; ++j) av[j] = qk_read(qb, rb, I0 + j);
             v16f sacc = (v16f){};
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < C::KS0; ++i) {
-                if (i + AHEAD < C::KS0) av[i + AHEAD] = qk_read(qa, ra, i + AHEAD);
-                if (C::EVEN || i < nks) sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[i]), qf[i], sacc);
-                if constexpr (do_dma)
-                    if (i < MAXK) dma_k(i);
+            for (int j = 0; j < N; ++j) {
+                if (j + AH < N) av[j + AH] = qk_read(qb, rb, I0 + j + AH);
+                sacc = mfma_bf16(__builtin_bit_cast(v8bf, av[j]), qf[j], sacc);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (do_dma) {
-#pragma unroll
-                for (int k = C::KS0; k < MAXK; ++k) dma_k(k);
-            }
-            const uint32_t so = sx_own0 + (uint32_t)(nblk_idx & 1) * SX_PAR;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-                lds_write16(so + 1024 * r4,
-                            __builtin_bit_cast(v4i, (v4f){sacc[4 * r4], sacc[4 * r4 + 1], sacc[4 * r4 + 2],
-                                                          sacc[4 * r4 + 3]}));
+            return sacc;
         };
 
-        if (nblk > 0) {
-            issue_block<C>(buf_of(0), kvb, lofs, w4, lane);
-            if (nblk > 1) issue_block<C>(buf_of(1), kvb, lofs + kBlk, w4, lane);
-            if (nblk > 1) wait_loads<C::LOADS_PER_WAVE>();
-            else wait_loads<0>();
-            land(0);
-            lds_barrier();  // block 0 visible
-            logits(0, 0, std::false_type{});
-            if (nblk > 1) {
-                wait_loads<0>();
-                land(1);
+        if (!main) {
+            // -------- second half of the logits, handed over; direct loads --------
+            const uint32_t sx_own = lds_addr(&sx[hg][0][lane]);
+            auto publish = [&](const v16f& sp) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    lds_write16(sx_own + r4 * (kWave * 16),
+                                __builtin_bit_cast(v4i, (v4f){sp[4 * r4], sp[4 * r4 + 1], sp[4 * r4 + 2],
+                                                              sp[4 * r4 + 3]}));
+            };
+            const int dw = hg;  // direct-load slot
+            auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
+                const uint32_t vm = rmask[blk % C::RING];
+                if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, dw, lane);
+            };
+            auto issue = [&](int blk) { issue_block<C>(buf_of(blk), kvb, rofs[blk % C::RING], dw, lane); };
+            if (nblk > 0) {
+                issue(0);
+                if (nblk > 1) issue(1);
+                if (nblk > 2) issue(2);
+                wait_blocks_left<C>(min(nblk, 3) - 1);
+                land(0);
+                lds_barrier();  // block 0 visible
+                publish(half_logits(0, std::false_type{}));
+                if (nblk > 1) {
+                    wait_blocks_left<C>(min(nblk, 3) - 2);
+                    land(1);
+                }
+                lds_barrier();  // mid-step of the prologue: block 1's rows visible
+                v16f sp = nblk > 1 ? half_logits(1, std::false_type{}) : (v16f){};
+                lds_barrier();  // end of the prologue
+                for (int blk = 0; blk < nblk; ++blk) {
+                    if (blk + 1 < nblk) publish(sp);  // block blk+1's half, computed in step blk-1
+                    const bool more = blk + 3 < nblk;
+                    if (more) issue(blk + 3);  // into the buffer block blk-1 used
+                    if (blk + 2 < nblk) {
+                        wait_blocks_left<C>(more ? 1 : 0);
+                        land(blk + 2);
+                    }
+                    lds_barrier();  // mid-step: block blk+2's rows visible
+                    // block blk+2's half, under wave w-4's softmax of block blk+1
+                    if (blk + 2 < nblk) sp = half_logits(blk + 2, std::false_type{});
+                    lds_barrier();  // end of step blk
+                }
             }
-            lds_barrier();  // block 0's partials and block 1's rows visible
+            lds_barrier();  // softmax denominators visible
+            return;
+        }
+
+        // -------- first half, the sum of both halves, and the softmax --------
+        const uint32_t sx_in = lds_addr(&sx[hg][0][lane]);
+        const uint32_t p_own = lds_addr(&pl[hg][0][lane]);
+        float m_run = -INFINITY;  // running max of the base-2 logits of this lane's head
+        float l_run = 0.f;        // running sum over this lane's half of the block rows
+        // Logits of block blk = own half + handed-over half (the same order in every step),
+        // empty slots at -inf, online softmax, P^T and rescale factors published.
+        auto softmax = [&](int blk, const v16f& s0) {
+            float z[16];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const v4f b = __builtin_bit_cast(v4f, lds_read16(sx_in + r4 * (kWave * 16)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z[4 * r4 + e] = s0[4 * r4 + e] + b[e];
+            }
+            const uint32_t vmask = rmask[blk % C::RING];
+            if (vmask != 0xffffffffu) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
+                    if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
+                }
+            }
+            // max as a tree of three-input maxima (written out: the compiler would quiet every
+            // input first), then across the lane halves with a lane swap instead of an LDS
+            // permute
+            auto mx = [](float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); };
+            const float t0 = max3f(z[0], z[1], z[2]), t1 = max3f(z[3], z[4], z[5]);
+            const float t2 = max3f(z[6], z[7], z[8]), t3 = max3f(z[9], z[10], z[11]);
+            const float t4 = max3f(z[12], z[13], z[14]);
+            const float m = max3f(max3f(t0, t1, t2), max3f(t3, t4, z[15]), t0);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+            const float mb = mx(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sm_log2;
+            // lazy running max: O is rescaled only when a block max exceeds it by more than
+            // kRescaleGap (alpha = 0 for the first block with a row, where O is still 0); both
+            // lane halves hold the same values
+            const bool bump = mb > m_run + kRescaleGap;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mb) : 1.f;
+            m_run = bump ? mb : m_run;
+            l_run *= alpha;
+            al[hg][mi] = alpha;
+            // p = 2^(sm_log2 * z - m_run); masked rows give exact zeros, also while no row has
+            // been seen (m_run = -inf is then replaced by 0)
+            const float mref = m_run == -INFINITY ? 0.f : m_run;
+            float ls = 0.f;
+            v8bf pf[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(z[8 * u + e], sm_log2, -mref));
+                    ls += pv;
+                    pf[u][e] = (__bf16)pv;
+                }
+            l_run += ls;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) lds_write16(p_own + u * (kWave * 16), __builtin_bit_cast(v4i, pf[u]));
+        };
+        if (nblk > 0) {
+            // wave 0 stages the row offsets of block b + RING during step b, from ids it loaded
+            // one step earlier (it issues no other global loads)
+            const bool stager = wv == 0;
+            int ids = stager && C::RING < nblk ? load_ids(C::RING) : -1;
+            lds_barrier();  // block 0 visible
+            v16f s0 = half_logits(0, std::true_type{});
+            lds_barrier();  // mid-step of the prologue: block 0's second half visible
+            softmax(0, s0);
+            lds_barrier();  // end of the prologue: block 0's P^T visible
             for (int blk = 0; blk < nblk; ++blk) {
-                if (blk + 1 < nblk) {
-                    if (blk + 2 < nblk) logits(blk + 1, blk + 2, std::true_type{});
-                    else logits(blk + 1, 0, std::false_type{});
+                if (stager && blk + C::RING < nblk) {
+                    stage(blk + C::RING, ids);
+                    ids = blk + C::RING + 1 < nblk ? load_ids(blk + C::RING + 1) : -1;
                 }
-                if (blk + 2 < nblk) {
-                    wait_loads<0>();
-                    land(blk + 2);
-                }
+                const bool next = blk + 1 < nblk;
+                if (next) s0 = half_logits(blk + 1, std::true_type{});
+                lds_barrier();  // mid-step: block blk+1's second half visible
+                if (next) softmax(blk + 1, s0);
                 lds_barrier();  // end of step blk
             }
+        }
+        const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+        const float l_tot = __uint_as_float(sl[0]) + __uint_as_float(sl[1]);
+        if (lane < 32) fin_l[hg][lane] = l_tot;
+        lds_barrier();  // softmax denominators visible
+        if (head >= H || lane >= 32) return;
+        if (!SPLIT) {
+            if (lse != nullptr)
+                lse[(int64_t)ri.qrow * H + head] =
+                    l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        } else {
+            part_ml[((int64_t)row * n_split + split) * H + head] = make_float2(m_run, l_tot);
         }
         return;
     }
 
-    // ---------------- softmax and value product ----------------
-    v16f oacc[C::VT0];
+    // ---------------- value product ----------------
+    const int vq = (wv & 1) + 2 * (wv >> 2);  // waves 2, 3, 6, 7 -> quarters 0..3
+    const bool active = vq < C::NVW;          // has value tiles
+    v16f oacc[2][C::VTW];
 #pragma unroll
-    for (int vt = 0; vt < C::VT0; ++vt) oacc[vt] = (v16f){};
-    float m_run = -INFINITY;  // running max of the base-2 logits of this lane's head
-    float l_run = 0.f;        // running sum over this lane's half of the block rows
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int t = 0; t < C::VTW; ++t) oacc[g][t] = (v16f){};
     // value operand (tr16 read) of 16-row slice u, row quad h, tile t at
-    // voff[u][h][t % TLV] + 64*TLV*(t / TLV); tr16 source lane j of each 16-lane group points
-    // at block row 16u + 8*half + j/4 (+4 for h = 1) and value columns cl*8 + sub/2 .. +3
-    uint32_t voff[2][2][C::TLV];
+    // voff[h][t % TLV] + 64*TLV*(t / TLV) + 16*PITCH*u (rows 16 apart have the same swizzle);
+    // tr16 source lane j of each 16-lane group points at block row 16u + 8*half + j/4 (+4 for
+    // h = 1) and value columns cl*8 + sub/2 .. +3
+    uint32_t voff[2][C::TLV];
     {
         const int vsub = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
         const int cl = vsub >> 3, sub = (vsub & 7) * 2;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int t = 0; t < C::TLV; ++t)
-                    voff[u][h][t] = RV::chunk(16 * u + 8 * half + (j16 >> 2) + 4 * h,
-                                              4 * (dp * C::VT0 + t) + cl) + sub;
+            for (int t = 0; t < C::TLV; ++t)
+                voff[h][t] = RV::chunk(8 * half + (j16 >> 2) + 4 * h, 4 * (vq * C::VTW + t) + cl) + sub;
     }
-    const uint32_t sx0 = lds_addr(&sx[0][hg][0][0][lane][0]);
-    const uint32_t sx1 = lds_addr(&sx[0][hg][1][0][lane][0]);
-    constexpr uint32_t SX_PAR = 2 * 2 * 4 * kWave * 4 * 4;  // bytes per parity
+    const uint32_t p_rd = lds_addr(&pl[0][0][lane]);
 
-    // Logits of block blk from the two published partials (the same sum in the same order in
-    // both value waves of a group, so both hold identical softmax state), masked rows, running
-    // max with lazy rescale of O, then P^T as the two bf16 B operands (slices u = 0, 1).
-    auto softmax = [&](int blk, v8bf (&pf)[2]) {
-        const uint32_t po = (uint32_t)(blk & 1) * SX_PAR;
-        float z[16];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const v4f a = __builtin_bit_cast(v4f, lds_read16(sx0 + po + 1024 * r4));
-            const v4f b = __builtin_bit_cast(v4f, lds_read16(sx1 + po + 1024 * r4));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[4 * r4 + e] = a[e] + b[e];
-        }
-        const uint32_t vmask = lmask[blk];
-        if (vmask != 0xffffffffu) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int slot = 16 * (r >> 3) + 8 * half + (r & 7);
-                if (!((vmask >> slot) & 1u)) z[r] = -INFINITY;
-            }
-        }
-        // max as a tree (med3(a, b, +inf) = max(a, b) for the non-NaN logits here; unlike
-        // fmaxf it needs no quieting of its inputs first), then across the lane halves with a
-        // lane swap instead of an LDS permute
-        auto mx = [](float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); };
-        float m8[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) m8[r] = mx(z[2 * r], z[2 * r + 1]);
-        float mb = mx(mx(mx(m8[0], m8[1]), mx(m8[2], m8[3])), mx(mx(m8[4], m8[5]), mx(m8[6], m8[7])));
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
-        mb = mx(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sm_log2;
-        const bool bump = mb > m_run + kRescaleGap;
-        if (__ballot(bump) != 0ull) {
-            const bool fresh = m_run == -INFINITY;
-            const float m_new = bump ? mb : m_run;
-            const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-            if (__ballot(!fresh) != 0ull) {
-                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // MFMA results settle
-#pragma unroll
-                for (int vt = 0; vt < C::VT0; ++vt) scale_agpr(oacc[vt], alpha);
-                asm volatile("s_nop 4" ::: "memory");  // before the next MFMA reads them
-            }
-        }
-        // p = 2^(sm_log2 * z - m_run); masked rows give exact zeros, also while no row has been
-        // seen (m_run = -inf is then replaced by 0)
-        const float mref = m_run == -INFINITY ? 0.f : m_run;
-        float ls = 0.f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(z[8 * u + e], sm_log2, -mref));
-                ls += pv;
-                pf[u][e] = (__bf16)pv;
-            }
-        l_run += ls;
-    };
-    // O^T += V^T P^T over this wave's value tiles.
-    auto values = [&](int blk, const v8bf (&pf)[2]) {
+    // One 16-row slice u of block blk: O^T += V^T P^T over this wave's value tiles, both head
+    // groups.
+    auto values = [&](int blk, int u, const v8bf (&pf)[2][2]) {
         const uint32_t cb = buf_of(blk);
-        uint32_t va_[2][2][C::TLV];
+        uint32_t va_[2][C::TLV];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int t = 0; t < C::TLV; ++t) va_[h][t] = opaque(cb + voff[h][t]);
+        v8bf va[C::VTW];
 #pragma unroll
-                for (int t = 0; t < C::TLV; ++t) va_[u][h][t] = opaque(cb + voff[u][h][t]);
-        auto vread = [&](int u, int t) {
-            const uint32_t imm = 64 * C::TLV * (t / C::TLV);
-            const v4s lo = ds_read_tr16(va_[u][0][t % C::TLV] + imm);
-            const v4s hi = ds_read_tr16(va_[u][1][t % C::TLV] + imm);
+        for (int t = 0; t < C::VTW; ++t) {
+            const uint32_t imm = 64 * C::TLV * (t / C::TLV) + 16 * RV::PITCH * u;
+            const v4s lo = ds_read_tr16(va_[0][t % C::TLV] + imm);
+            const v4s hi = ds_read_tr16(va_[1][t % C::TLV] + imm);
             const v2i l2 = __builtin_bit_cast(v2i, lo), h2 = __builtin_bit_cast(v2i, hi);
-            return __builtin_bit_cast(v8bf, (v4i){l2.x, l2.y, h2.x, h2.y});
-        };
-        v8bf va[2][C::VT0];
-#pragma unroll
-        for (int t = 0; t < C::VT0; ++t) va[0][t] = vread(0, t);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < C::VT0; ++t) {
-            va[1][t] = vread(1, t);
-            oacc[t] = mfma_bf16(va[0][t], pf[0], oacc[t]);
-            __builtin_amdgcn_sched_barrier(0);
+            va[t] = __builtin_bit_cast(v8bf, (v4i){l2.x, l2.y, h2.x, h2.y});
         }
 #pragma unroll
-        for (int t = 0; t < C::VT0; ++t) oacc[t] = mfma_bf16(va[1][t], pf[1], oacc[t]);
+        for (int t = 0; t < C::VTW; ++t) {
+            oacc[0][t] = mfma_bf16(va[t], pf[0][u], oacc[0][t]);
+            oacc[1][t] = mfma_bf16(va[t], pf[1][u], oacc[1][t]);
+        }
 #pragma unroll
-        for (int vt = 0; vt < C::VT0; ++vt) pin_agpr(oacc[vt]);
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int t = 0; t < C::VTW; ++t) pin_agpr(oacc[g][t]);
     };
+    // P^T of block blk for both groups, and the rescale of O its softmax asked for.
+    auto take_p = [&](v8bf (&pf)[2][2]) {
+        const float a0 = al[0][mi], a1 = al[1][mi];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                pf[g][u] = __builtin_bit_cast(v8bf, lds_read16(p_rd + (2 * g + u) * (kWave * 16)));
+        if (__ballot(a0 != 1.f || a1 != 1.f) != 0ull) {
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");  // MFMA results settle
+#pragma unroll
+            for (int t = 0; t < C::VTW; ++t) {
+                scale_agpr(oacc[0][t], a0);
+                scale_agpr(oacc[1][t], a1);
+            }
+            asm volatile("s_nop 4" ::: "memory");  // before the next MFMA reads them
+        }
+    };
+    if (!active) {  // only the barriers
+        if (nblk > 0)
+            for (int b = 0; b < 2 * nblk + 3; ++b) lds_barrier();
+        lds_barrier();
+        return;
+    }
     if (nblk > 0) {
         lds_barrier();  // block 0 visible
-        lds_barrier();  // block 0's partials and block 1's rows visible
+        lds_barrier();  // mid-step of the prologue
+        lds_barrier();  // end of the prologue: block 0's P^T visible
         for (int blk = 0; blk < nblk; ++blk) {
-            v8bf pf[2];
-            softmax(blk, pf);
-            values(blk, pf);
+            v8bf pf[2][2];
+            take_p(pf);
+            values(blk, 0, pf);
+            lds_barrier();  // mid-step
+            values(blk, 1, pf);
             lds_barrier();  // end of step blk
         }
     }
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    lds_barrier();  // softmax denominators visible
 
     // ---- epilogue ----
-    if (head >= H) return;
-    if (!SPLIT) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* op = out + ((int64_t)ri.qrow * H + head) * DV;
 #pragma unroll
-        for (int t = 0; t < C::VT0; ++t)
+    for (int g = 0; g < 2; ++g) {
+        const int head = hh * 64 + g * 32 + mi;
+        if (head >= H) continue;
+        if (!SPLIT) {
+            const float l_tot = fin_l[g][mi];
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            uint16_t* op = out + ((int64_t)ri.qrow * H + head) * DV;
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int v = 32 * (dp * C::VT0 + t) + 8 * rb + 4 * half;
-                const uint32_t w0 = (uint32_t)f2bf(oacc[t][4 * rb + 0] * inv) |
-                                    ((uint32_t)f2bf(oacc[t][4 * rb + 1] * inv) << 16);
-                const uint32_t w1 = (uint32_t)f2bf(oacc[t][4 * rb + 2] * inv) |
-                                    ((uint32_t)f2bf(oacc[t][4 * rb + 3] * inv) << 16);
-                *(v2i*)(op + v) = (v2i){(int)w0, (int)w1};
-            }
-        if (lse != nullptr && half == 0 && dp == 0)
-            lse[(int64_t)ri.qrow * H + head] =
-                l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    } else {
-        const int64_t item = (int64_t)row * n_split + split;
-        float* op = part_o + (item * H + head) * DV;
+            for (int t = 0; t < C::VTW; ++t)
 #pragma unroll
-        for (int t = 0; t < C::VT0; ++t)
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int v = 32 * (vq * C::VTW + t) + 8 * rb + 4 * half;
+                    const uint32_t w0 = (uint32_t)f2bf(oacc[g][t][4 * rb + 0] * inv) |
+                                        ((uint32_t)f2bf(oacc[g][t][4 * rb + 1] * inv) << 16);
+                    const uint32_t w1 = (uint32_t)f2bf(oacc[g][t][4 * rb + 2] * inv) |
+                                        ((uint32_t)f2bf(oacc[g][t][4 * rb + 3] * inv) << 16);
+                    *(v2i*)(op + v) = (v2i){(int)w0, (int)w1};
+                }
+        } else {
+            const int64_t item = (int64_t)row * n_split + split;
+            float* op = part_o + (item * H + head) * DV;
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int v = 32 * (dp * C::VT0 + t) + 8 * rb + 4 * half;
-                *(v4f*)(op + v) = (v4f){oacc[t][4 * rb + 0], oacc[t][4 * rb + 1],
-                                        oacc[t][4 * rb + 2], oacc[t][4 * rb + 3]};
-            }
-        if (half == 0 && dp == 0) part_ml[item * H + head] = make_float2(m_run, l_tot);
+            for (int t = 0; t < C::VTW; ++t)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int v = 32 * (vq * C::VTW + t) + 8 * rb + 4 * half;
+                    *(v4f*)(op + v) = (v4f){oacc[g][t][4 * rb + 0], oacc[g][t][4 * rb + 1],
+                                            oacc[g][t][4 * rb + 2], oacc[g][t][4 * rb + 3]};
+                }
+        }
     }
 }
 
