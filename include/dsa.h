@@ -102,9 +102,19 @@ dsa_status dsa_indexer_scores(const dsa_dims* dims, const dsa_batch* batch, cons
  * on fine-grained token selection: only the k best-scoring positions are kept).
  * Ranking: larger first, -0 equals +0, NaN below -inf, equal scores -> lower position first.
  * idx [T, topk] int32 receives the selected positions in ascending order followed by -1
- * in the unused slots.  The result is unique, so it is bit-exact and deterministic. */
+ * in the unused slots.  The result is unique, so it is bit-exact and deterministic.
+ *   ws / ws_bytes: optional workspace (NULL/0 allowed, else 16-byte aligned).  With at least
+ *   dsa_topk_workspace_size bytes (non-zero only for batches of fewer than 128 rows, e.g.
+ *   decode) each row is split over several workgroups; otherwise one workgroup selects each
+ *   row.  The result is the same.  The workspace is scratch owned by the caller; its
+ *   contents are undefined afterwards. */
 dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* scores,
-                    int64_t score_stride, int32_t* idx, hipStream_t stream);
+                    int64_t score_stride, int32_t* idx, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Workspace that lets dsa_topk split rows over several workgroups for this batch (0 when
+ * the batch has 128 rows or more, or rows longer than 131072 scores). */
+dsa_status dsa_topk_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
 
 /* Sparse MQA over the latent cache (stage 3).
  * For query row i and head h, over the slots of idx[i,:] that are not -1 (positions in

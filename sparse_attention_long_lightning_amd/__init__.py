@@ -100,7 +100,8 @@ def lib():
             "dsa_workspace_size": [P, P, P],
             "dsa_workspace_min": [P, P, P],
             "dsa_indexer_scores": [P, P, P, P, P, P, P, P, I64, P],
-            "dsa_topk": [P, P, P, I64, P, P],
+            "dsa_topk": [P, P, P, I64, P, P, S, P],
+            "dsa_topk_workspace_size": [P, P, P],
             "dsa_sparse_mqa": [P, P, P, P, P, P, P, P, S, P],
             "dsa_forward": [P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
         }.items():
@@ -158,10 +159,21 @@ def indexer_scores(dims, batch: Batch, q8, q_scale, w, k8, k_scale, scores, scor
     return scores
 
 
-def topk(dims, batch: Batch, scores, score_stride: int, idx, stream=None):
+def topk_workspace_size(dims, batch: Batch) -> int:
+    out = ctypes.c_size_t(0)
     d = _dims(dims)
+    _check(lib().dsa_topk_workspace_size(ctypes.byref(d), ctypes.byref(batch.c), ctypes.byref(out)),
+           "dsa_topk_workspace_size")
+    return int(out.value)
+
+
+def topk(dims, batch: Batch, scores, score_stride: int, idx, ws=None, stream=None):
+    """ws: optional uint8 device tensor of at least topk_workspace_size bytes (rows are then
+    split over several workgroups); None selects each row with one workgroup."""
+    d = _dims(dims)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().dsa_topk(ctypes.byref(d), ctypes.byref(batch.c), _ptr(scores), int(score_stride),
-                          _ptr(idx), _stream(stream)), "dsa_topk")
+                          _ptr(idx), _ptr(ws), ws_bytes, _stream(stream)), "dsa_topk")
     return idx
 
 

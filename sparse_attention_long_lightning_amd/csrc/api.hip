@@ -98,25 +98,25 @@ dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_
 struct ForwardPlan {
     int64_t stride = 0;
     int chunk = 0;  // prefill rows per pass
-    size_t scores_off = 0, idx_off = 0, mqa_off = 0, total = 0;
+    size_t scores_off = 0, idx_off = 0, tail_off = 0, topk_bytes = 0, total = 0;
 };
 
-// Workspace layout of dsa_forward: [scores | idx (when idx_out is NULL) | MQA partials].
+// Workspace layout of dsa_forward: [scores | idx (when idx_out is NULL) | tail], where the
+// tail holds the top-k candidates and, later on the same stream, the MQA split partials.
 ForwardPlan plan_forward(const dsa_dims* d, Shape shape, const Batch& bt, int chunk) {
     ForwardPlan p;
     p.stride = score_stride_for(bt);
+    p.chunk = bt.decode ? bt.T : chunk;
+    p.scores_off = 0;
+    p.idx_off = align_up((size_t)p.chunk * p.stride * sizeof(float));
+    p.tail_off = p.idx_off + align_up((size_t)p.chunk * d->topk * sizeof(int32_t));
+    p.topk_bytes = topk_ws_bytes(p.chunk, bt.max_lk, d->topk);
+    size_t tail = p.topk_bytes;
     if (bt.decode) {
-        p.chunk = bt.T;
-        p.scores_off = 0;
-        p.idx_off = align_up((size_t)bt.T * p.stride * sizeof(float));
-        p.mqa_off = p.idx_off + align_up((size_t)bt.T * d->topk * sizeof(int32_t));
-        p.total = p.mqa_off + mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, d->topk));
-    } else {
-        p.chunk = chunk;
-        p.idx_off = align_up((size_t)chunk * p.stride * sizeof(float));
-        p.mqa_off = p.idx_off + align_up((size_t)chunk * d->topk * sizeof(int32_t));
-        p.total = p.mqa_off;
+        const size_t mqa = mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, d->topk));
+        if (mqa > tail) tail = mqa;
     }
+    p.total = p.tail_off + align_up(tail);
     return p;
 }
 
@@ -148,10 +148,7 @@ dsa_status dsa_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size
     if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
     if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
     const ForwardPlan p = plan_forward(dims, shape, bt, default_chunk(bt));
-    size_t need = p.total;
-    const size_t mqa = mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, dims->topk));
-    if (mqa > need) need = mqa;
-    *bytes = need;
+    *bytes = p.total;
     return DSA_OK;
 }
 
@@ -164,10 +161,7 @@ dsa_status dsa_workspace_min(const dsa_dims* dims, const dsa_batch* batch, size_
     if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
     const int c = bt.max_lq < kRowGranule ? (bt.max_lq < 1 ? 1 : bt.max_lq) : kRowGranule;
     const ForwardPlan p = plan_forward(dims, shape, bt, c);
-    size_t need = p.total;
-    const size_t mqa = mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, dims->topk));
-    if (mqa > need) need = mqa;
-    *bytes = need;
+    *bytes = p.total;
     return DSA_OK;
 }
 
@@ -200,8 +194,19 @@ dsa_status dsa_indexer_scores(const dsa_dims* dims, const dsa_batch* batch, cons
     return DSA_OK;
 }
 
+dsa_status dsa_topk_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if (bytes == nullptr) return DSA_ERR_INVALID_ARG;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    *bytes = topk_ws_bytes(bt.T, bt.max_lk, dims->topk);
+    return DSA_OK;
+}
+
 dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* scores,
-                    int64_t score_stride, int32_t* idx, hipStream_t stream) {
+                    int64_t score_stride, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
     Shape shape;
     Batch bt;
     dsa_status st;
@@ -210,8 +215,10 @@ dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* s
     if (bt.T == 0) return DSA_OK;
     if (!scores || !idx || !aligned16(scores) || !aligned16(idx)) return DSA_ERR_INVALID_ARG;
     if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
+    if (ws != nullptr && !aligned16(ws)) return DSA_ERR_WORKSPACE;
     RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
-    return hip_status(launch_topk(scores, score_stride, idx, dims->topk, map, bt.T, stream));
+    return hip_status(launch_topk(scores, score_stride, idx, dims->topk, map, bt.T, bt.max_lk, ws,
+                                  ws == nullptr ? 0 : ws_bytes, stream));
 }
 
 dsa_status dsa_sparse_mqa(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
@@ -269,18 +276,17 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
             fprintf(stderr, "[dsa] decode B=%d max_len_k=%d stride=%lld splits=%d\n", bt.B, bt.max_lk,
                     (long long)p.stride, n_split);
         hipError_t e = launch_indexer_decode(ia, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, stream);
-        if (e == hipSuccess) e = launch_topk(sc, p.stride, ix, topk, map, bt.T, stream);
-        if (e == hipSuccess) e = launch_sparse_mqa(ma, map, bt.T, n_split, wsb + p.mqa_off, stream);
+        if (e == hipSuccess)
+            e = launch_topk(sc, p.stride, ix, topk, map, bt.T, bt.max_lk, wsb + p.tail_off, p.topk_bytes, stream);
+        if (e == hipSuccess) e = launch_sparse_mqa(ma, map, bt.T, n_split, wsb + p.tail_off, stream);
         return hip_status(e);
     }
 
     // Prefill: passes of `chunk` query rows per sequence.
     const int64_t stride = score_stride_for(bt);
-    auto bytes_for = [&](int c) {
-        return align_up((size_t)c * stride * sizeof(float)) +
-               (idx_out ? 0 : align_up((size_t)c * topk * sizeof(int32_t)));
-    };
-    const size_t per_row = (size_t)stride * sizeof(float) + (idx_out ? 0 : (size_t)topk * 4);
+    // the idx area is reserved even when idx_out is given (plan_forward's layout)
+    auto bytes_for = [&](int c) { return plan_forward(dims, shape, bt, c).total; };
+    const size_t per_row = (size_t)stride * sizeof(float) + (size_t)topk * 4 + topk_ws_bytes(1, bt.max_lk, topk);
     int64_t c64 = (int64_t)(ws_bytes / per_row);
     int chunk = (int)(c64 < bt.max_lq ? c64 : bt.max_lq);
     if (chunk > kRowGranule) chunk -= chunk % kRowGranule;
@@ -309,7 +315,9 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
                                            sc + (int64_t)(rsel - r0) * p.stride, stream);
             int32_t* ix = idx_out ? idx_out + (int64_t)(qb + r0) * topk : ix_ws;
             RowMap map{nullptr, nullptr, 1, qb + r0, pos0 + r0, kb};
-            if (e == hipSuccess) e = launch_topk(sc, p.stride, ix, topk, map, r1 - r0, stream);
+            if (e == hipSuccess)
+                e = launch_topk(sc, p.stride, ix, topk, map, r1 - r0, pos0 + r1, wsb + p.tail_off, p.topk_bytes,
+                                stream);
             MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale};
             if (e == hipSuccess) e = launch_sparse_mqa(ma, map, r1 - r0, 1, nullptr, stream);
             if (e != hipSuccess) return DSA_ERR_HIP;

@@ -31,8 +31,13 @@ hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,
                                  const int32_t* cu_q, const int32_t* cu_k, hipStream_t st);
 
 // Top-k over n_rows score rows; row i reads scores + i * stride and writes idx + i * topk.
+// With a workspace of topk_ws_bytes(n_rows, max_len, topk) bytes (max_len = the longest
+// row) rows are split over several workgroups; without one (or for rows too long for the
+// split) one workgroup selects each row.  Both give the same result.
+size_t topk_ws_bytes(int n_rows, int max_len, int topk);
 hipError_t launch_topk(const float* scores, int64_t stride, int32_t* idx, int topk,
-                       const RowMap& map, int n_rows, hipStream_t st);
+                       const RowMap& map, int n_rows, int max_len, void* ws, size_t ws_bytes,
+                       hipStream_t st);
 
 struct MqaArgs {
     Shape shape;

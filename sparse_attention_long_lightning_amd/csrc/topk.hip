@@ -67,7 +67,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total
 
 // Finds bin b of an LDS histogram with count(bins > b) < need <= count(bins >= b).
 // Requires 1 <= need <= total count.  Result in sm.sel_bin / sm.sel_above.
-__device__ void find_threshold(const uint32_t* hist, int nb, int need, Smem& sm) {
+template <class S>
+__device__ void find_threshold(const uint32_t* hist, int nb, int need, S& sm) {
     if (threadIdx.x == 0) {  // defined result even if no bin qualifies (ordered by the scan's barrier)
         sm.sel_bin = 0;
         sm.sel_above = 0;
@@ -361,13 +362,313 @@ __global__ __launch_bounds__(kThreads, 2) void topk_kernel(const float* __restri
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Segmented selection: several workgroups per row.
+//
+// Under the total order "larger key first, lower position first among equal keys" the
+// selected set is the first k elements of the row.  An element among the first k of its
+// row is also among the first k of any part of the row that holds it (fewer elements
+// precede it there), so the selection equals the first k of the union of every segment's
+// own first k.  The segment kernel keeps a segment of kSeg scores in LDS, reads it from
+// memory once and writes its first k as (key, position) candidates in position order; the
+// merge kernel selects the row's first k among at most kMaxSegs * k candidates.  Both give
+// the same unique result as the single-workgroup kernel above.
+constexpr int kSeg = 16384;   // scores per segment workgroup (64 KiB of keys in LDS)
+constexpr int kMaxSegs = 8;   // segments per row the merge holds in LDS
+// Fewer rows than this are split (one workgroup per row would leave most CUs idle); with
+// more, one workgroup per row is faster, as it keeps no candidates in memory.
+constexpr int kSplitRows = 128;
+
+struct SelSmem {
+    uint32_t hist[kBins1];
+    int wsum[kWaves];
+    int wgt[kWaves], weq[kWaves];
+    int sel_bin, sel_above;
+};
+
+// Among keys[0..m) in LDS, the kk-th largest key theta (1 <= kk <= m) and the number of
+// keys above it.  Radix select over the keys' actual range [lo, hi]: each pass splits the
+// current range into 2048 bins (11 bits of key - lo), so at most three passes reach a
+// single key value.  keys must hold m rounded up to a multiple of 4 entries (16-byte reads).
+__device__ void lds_kth_key(const uint32_t* keys, int m, int kk, SelSmem& sm, uint32_t& theta,
+                            int& above) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint4* k4 = (const uint4*)keys;
+    const int m4 = (m + 3) >> 2;
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int i = tid; i < m4; i += kThreads) {
+        const uint4 v = k4[i];
+        const uint32_t k[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (4 * i + c < m) {
+                lo = min(lo, k[c]);
+                hi = max(hi, k[c]);
+            }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+    }
+    if (lane == 0) {
+        sm.wgt[wv] = (int)lo;
+        sm.weq[wv] = (int)hi;
+    }
+    __syncthreads();
+    lo = 0xffffffffu;
+    hi = 0u;
+    for (int w = 0; w < kWaves; ++w) {
+        lo = min(lo, (uint32_t)sm.wgt[w]);
+        hi = max(hi, (uint32_t)sm.weq[w]);
+    }
+    __syncthreads();
+    // the kk-th key lies in [lo, lo + lim]; `ab` keys lie above that range
+    uint32_t lim = hi - lo;
+    int need = kk, ab = 0;
+    while (lim > 0) {
+        const int bits = 32 - __clz(lim);
+        const int sh = bits > 11 ? bits - 11 : 0;
+        for (int j = tid; j < kBins1; j += kThreads) sm.hist[j] = 0u;
+        __syncthreads();
+        for (int i = tid; i < m4; i += kThreads) {
+            const uint4 v = k4[i];
+            const uint32_t k[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t d = k[c] - lo;
+                if (4 * i + c < m && d <= lim) atomicAdd(&sm.hist[d >> sh], 1u);
+            }
+        }
+        __syncthreads();
+        find_threshold(sm.hist, kBins1, need, sm);
+        const uint32_t b = (uint32_t)sm.sel_bin;
+        const int a = sm.sel_above;
+        __syncthreads();
+        ab += a;
+        need -= a;
+        lo += b << sh;
+        lim = min(lim - (b << sh), (1u << sh) - 1u);
+    }
+    theta = lo;
+    above = ab;
+}
+
+// Number of set bits of ballot b in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t b) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// Emits, in position order, the keys[0..m) above theta and the first need_eq equal to it.
+// Wave w owns a contiguous range of 256-element groups; lane l of a group holds its 4
+// consecutive elements 4l .. 4l+3 (one 16-byte LDS read).  emit(j, key, slot) is called for
+// the element j taking output slot `slot`.  keys must hold m rounded up to a multiple of 4.
+template <class F>
+__device__ void emit_ordered(const uint32_t* keys, int m, uint32_t theta, int need_eq, SelSmem& sm,
+                             F&& emit) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint4* k4 = (const uint4*)keys;
+    const int ngrp = (m + 255) >> 8;
+    const int per = (ngrp + kWaves - 1) / kWaves;
+    const int g0 = min(ngrp, wv * per), g1 = min(ngrp, g0 + per);
+    auto load = [&](int g, uint32_t (&k)[4], bool (&in)[4]) {
+        const int j = (g << 8) + 4 * lane;
+        const uint4 v = j < m ? k4[j >> 2] : make_uint4(0u, 0u, 0u, 0u);
+        k[0] = v.x;
+        k[1] = v.y;
+        k[2] = v.z;
+        k[3] = v.w;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) in[c] = j + c < m;
+    };
+    int gt = 0, eq = 0;
+    for (int g = g0; g < g1; ++g) {
+        uint32_t k[4];
+        bool in[4];
+        load(g, k, in);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            gt += __popcll(__ballot(in[c] && k[c] > theta));
+            eq += __popcll(__ballot(in[c] && k[c] == theta));
+        }
+    }
+    if (lane == 0) {
+        sm.wgt[wv] = gt;
+        sm.weq[wv] = eq;
+    }
+    __syncthreads();
+    int eq_run = 0, out_run = 0;
+    for (int w = 0; w < wv; ++w) {
+        const int e = sm.weq[w];
+        out_run += sm.wgt[w] + min(e, max(0, need_eq - eq_run));
+        eq_run += e;
+    }
+    for (int g = g0; g < g1; ++g) {
+        uint32_t k[4];
+        bool in[4];
+        load(g, k, in);
+        bool e[4], sel[4];
+        uint64_t be[4], bs[4];
+        int r = eq_run;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            e[c] = in[c] && k[c] == theta;
+            be[c] = __ballot(e[c]);
+            r += lanes_below(be[c]);
+        }
+        int ne = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            ne += __popcll(be[c]);
+            sel[c] = in[c] && (k[c] > theta || (e[c] && r < need_eq));
+            r += e[c] ? 1 : 0;
+        }
+        int slot = out_run, ns = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bs[c] = __ballot(sel[c]);
+            slot += lanes_below(bs[c]);
+            ns += __popcll(bs[c]);
+        }
+        const int j = (g << 8) + 4 * lane;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (sel[c]) emit(j + c, k[c], slot++);
+        out_run += ns;
+        eq_run += ne;
+    }
+}
+
+// Candidates of row r, segment g: cand_key / cand_pos + (r * n_segs + g) * topk, min(topk,
+// segment length) of them, in position order.
+__global__ __launch_bounds__(kThreads, 2) void topk_segment_kernel(
+    const float* __restrict__ scores, int64_t stride, int topk, RowMap map, int n_rows, int n_segs,
+    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_pos) {
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kSeg];
+    __shared__ SelSmem sm;
+    const int g = blockIdx.x, row = blockIdx.y;
+    if (row >= n_rows) return;
+    const RowInfo ri = row_info(map, row);
+    const int n = ri.pos + 1;
+    const int s0 = g * kSeg;
+    if (n <= topk || s0 >= n) return;  // the merge handles short rows
+    const int m = min(kSeg, n - s0);
+    const int tid = threadIdx.x;
+    const float* x = scores + (int64_t)row * stride + s0;
+    {
+        // all of this thread's pieces are loaded before any is stored, so the whole segment
+        // is in flight at once
+        constexpr int NP = kSeg / (4 * kThreads);
+        uint32_t k[NP][4];
+        bool ok[NP][4];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) load4(x, 4 * (tid + u * kThreads), m, k[u], ok[u]);
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            const int e = 4 * (tid + u * kThreads);
+            if (ok[u][3]) *(uint4*)&keys[e] = make_uint4(k[u][0], k[u][1], k[u][2], k[u][3]);
+            else
+                for (int c = 0; c < 4; ++c)
+                    if (ok[u][c]) keys[e + c] = k[u][c];
+        }
+    }
+    __syncthreads();
+    const int64_t base = ((int64_t)row * n_segs + g) * topk;
+    uint32_t* ck = cand_key + base;
+    int32_t* cp = cand_pos + base;
+    if (m <= topk) {  // the whole segment is a candidate set
+        for (int j = tid; j < m; j += kThreads) {
+            ck[j] = keys[j];
+            cp[j] = s0 + j;
+        }
+        return;
+    }
+    uint32_t theta;
+    int above;
+    lds_kth_key(keys, m, topk, sm, theta, above);
+    emit_ordered(keys, m, theta, topk - above, sm, [&](int j, uint32_t key, int slot) {
+        ck[slot] = key;
+        cp[slot] = s0 + j;
+    });
+}
+
+__global__ __launch_bounds__(kThreads, 1) void topk_merge_kernel(
+    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos, int32_t* __restrict__ idx,
+    int topk, RowMap map, int n_rows, int n_segs) {
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kMaxSegs * kMaxTopk];
+    __shared__ __attribute__((aligned(16))) int32_t pos[kMaxSegs * kMaxTopk];
+    __shared__ SelSmem sm;
+    const int row = blockIdx.x;
+    if (row >= n_rows) return;
+    const RowInfo ri = row_info(map, row);
+    const int n = ri.pos + 1;
+    int32_t* out = idx + (int64_t)row * topk;
+    const int tid = threadIdx.x;
+    if (n <= topk) {  // every candidate is selected
+        for (int j = tid; j < topk; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    // every segment but the last holds exactly topk candidates (kSeg >= topk), so the row's
+    // candidates are one contiguous run
+    const int nseg = (n + kSeg - 1) / kSeg;
+    const int total = (nseg - 1) * topk + min(topk, n - (nseg - 1) * kSeg);
+    const uint32_t* ck = cand_key + (int64_t)row * n_segs * topk;
+    const int32_t* cp = cand_pos + (int64_t)row * n_segs * topk;
+    constexpr int U = 8;
+    for (int e0 = tid; e0 < total; e0 += U * kThreads) {
+        uint32_t kv[U];
+        int32_t pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * kThreads;
+            kv[u] = e < total ? ck[e] : 0u;
+            pv[u] = e < total ? cp[e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * kThreads;
+            if (e < total) {
+                keys[e] = kv[u];
+                pos[e] = pv[u];
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t theta;
+    int above;
+    lds_kth_key(keys, total, topk, sm, theta, above);
+    emit_ordered(keys, total, theta, topk - above, sm, [&](int j, uint32_t, int slot) { out[slot] = pos[j]; });
+}
+
 }  // namespace
 
+int topk_segments(int max_len) { return (max_len + kSeg - 1) / kSeg; }
+
+size_t topk_ws_bytes(int n_rows, int max_len, int topk) {
+    const int ns = topk_segments(max_len);
+    if (ns > kMaxSegs || n_rows <= 0 || n_rows >= kSplitRows) return 0;
+    return (size_t)n_rows * ns * topk * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
 hipError_t launch_topk(const float* scores, int64_t stride, int32_t* idx, int topk,
-                       const RowMap& map, int n_rows, hipStream_t st) {
+                       const RowMap& map, int n_rows, int max_len, void* ws, size_t ws_bytes,
+                       hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3(n_rows), dim3(kThreads), 0, st, scores, stride, idx, topk,
-                       map, n_rows);
+    const size_t need = topk_ws_bytes(n_rows, max_len, topk);
+    if (need == 0 || ws == nullptr || ws_bytes < need) {
+        hipLaunchKernelGGL(topk_kernel, dim3(n_rows), dim3(kThreads), 0, st, scores, stride, idx, topk,
+                           map, n_rows);
+        return hipGetLastError();
+    }
+    const int ns = topk_segments(max_len);
+    uint32_t* ck = (uint32_t*)ws;
+    int32_t* cp = (int32_t*)(ck + (size_t)n_rows * ns * topk);
+    hipLaunchKernelGGL(topk_segment_kernel, dim3(ns, n_rows), dim3(kThreads), 0, st, scores, stride, topk,
+                       map, n_rows, ns, ck, cp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(n_rows), dim3(kThreads), 0, st, ck, cp, idx, topk, map,
+                       n_rows, ns);
     return hipGetLastError();
 }
 

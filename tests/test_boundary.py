@@ -90,9 +90,11 @@ def test_null_and_misaligned_pointers():
     assert call_forward(d, b, idx=FAKE + 2) == INVALID
     assert call_forward(d, b, ws=None) == WORKSPACE
     lib = dsa.lib()
-    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 64, None, None) == INVALID
-    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 60, FAKE, None) == INVALID  # stride < len
-    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 66, FAKE, None) == INVALID  # not x4
+    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 64, None, None, 0, None) == INVALID
+    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 60, FAKE, None, 0, None) == INVALID  # stride < len
+    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 66, FAKE, None, 0, None) == INVALID  # not x4
+    assert lib.dsa_topk(ctypes.byref(d), ctypes.byref(b.c), FAKE, 64, FAKE, FAKE + 4, 1 << 20,
+                        None) == WORKSPACE  # misaligned workspace
     assert lib.dsa_indexer_scores(ctypes.byref(d), ctypes.byref(b.c), FAKE, FAKE, FAKE, FAKE, FAKE,
                                   FAKE + 4, 64, None) == INVALID
     assert lib.dsa_sparse_mqa(ctypes.byref(d), ctypes.byref(b.c), FAKE, FAKE, None, FAKE, None, None,
@@ -125,3 +127,15 @@ def test_empty_batch_is_a_no_op():
     d = dims_with()
     b = cpu_batch([0, 0], [0, 100])
     assert call_forward(d, b, ptr=None, ws_bytes=0) == OK
+
+
+def test_topk_workspace_covers_the_segment_candidates():
+    d = dims_with()
+    # 32 one-query sequences, the longest 91,529 keys: six 16K-score segments per row, each
+    # keeping k (key, position) candidates of 8 bytes
+    db = cpu_batch(list(range(33)), [0] + [91529 * (i + 1) for i in range(32)])
+    assert dsa.topk_workspace_size(d, db) == 32 * 6 * 2048 * 8
+    # rows longer than eight segments, or batches of 128 rows and more, are selected by one
+    # workgroup per row: no workspace
+    assert dsa.topk_workspace_size(d, cpu_batch([0, 1], [0, 8 * 16384 + 1])) == 0
+    assert dsa.topk_workspace_size(d, cpu_batch([0, 128], [0, 5000])) == 0

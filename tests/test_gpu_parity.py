@@ -132,12 +132,31 @@ def adversarial_rows(k, rng):
     rows.append(bits.view(np.float32).astype(np.float64))   # random fp32 bit patterns (incl. NaN)
     rows.append(rng.normal(size=131072) * 1e-3)             # longest prefill row
     rows.append(np.abs(rng.normal(size=50000)) + 10.0)      # one exponent range
+    rows.append(np.full(70000, 2.0))                        # ties across five 16K segments
+    x = rng.normal(size=50000)
+    x[rng.permutation(50000)[:6000]] = np.sort(x)[-1000]    # threshold ties in every segment
+    rows.append(x)
+    rows.append(rng.normal(size=16384))                     # one full segment
+    rows.append(rng.normal(size=16385))                     # a segment plus one element
+    x = rng.normal(size=40000)
+    x[16384 - 3000:16384 + 3000] = 7.0                      # a tie block across a boundary
+    rows.append(x)
     return [r.astype(np.float32) for r in rows]
 
 
+def topk_ws(dims, batch, split, cuda):
+    """Workspace for the segmented path (split=True) or None (one workgroup per row)."""
+    if not split:
+        return None
+    n = dsa.topk_workspace_size(dims, batch)
+    assert n > 0
+    return torch.empty(n, dtype=torch.uint8, device=cuda)
+
+
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("k", [2048, 32, 1])
-def test_topk_bit_exact_on_identical_arrays(cuda, k):
-    say(f"topk adversarial rows k={k}")
+def test_topk_bit_exact_on_identical_arrays(cuda, k, split):
+    say(f"topk adversarial rows k={k} split={split}")
     rng = np.random.default_rng(7 + k)
     rows = adversarial_rows(max(k, 4), rng)
     lens = [len(r) for r in rows]
@@ -151,7 +170,7 @@ def test_topk_bit_exact_on_identical_arrays(cuda, k):
     batch = dsa.Batch(cu_q, cu_k, device=cuda)
     scores = torch.from_numpy(buf).to(cuda)
     idx = torch.empty(len(rows), k, dtype=torch.int32, device=cuda)
-    dsa.topk(dims, batch, scores, stride, idx)
+    dsa.topk(dims, batch, scores, stride, idx, ws=topk_ws(dims, batch, split, cuda))
     torch.cuda.synchronize()
     ref = oracle.topk_rows(rows, k)
     got = idx.cpu().numpy()
@@ -174,6 +193,26 @@ def test_topk_prefill_rows_with_shortcut(cuda):
     ref = oracle.topk_rows([buf[r, : r + 1] for r in rows], k)
     for i, r in enumerate(rows):
         assert np.array_equal(got[r], ref[i]), f"row {r}"
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_topk_few_prefill_rows(cuda, split):
+    say(f"topk 120 rows of two sequences (one of them all below k) split={split}")
+    k = 2048
+    rng = np.random.default_rng(12)
+    lq, lk = [60, 60], [60, 30000]
+    stride = stride_for(max(lk))
+    buf = rng.normal(size=(sum(lq), stride)).astype(np.float32)
+    dims = dsa.Dims(64, 128, k, 128, 576, 512, 0.07)
+    batch = dsa.Batch([0, 60, 120], [0, 60, 30060], device=cuda)
+    idx = torch.empty(sum(lq), k, dtype=torch.int32, device=cuda)
+    dsa.topk(dims, batch, torch.from_numpy(buf).to(cuda), stride, idx, ws=topk_ws(dims, batch, split, cuda))
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    rows = [buf[i, : i + 1] for i in range(60)] + [buf[60 + i, : lk[1] - lq[1] + i + 1] for i in range(60)]
+    ref = oracle.topk_rows(rows, k)
+    for i in range(120):
+        assert np.array_equal(got[i], ref[i]), f"row {i}"
 
 
 # ------------------------------------------------------------------ sparse MQA ------------
