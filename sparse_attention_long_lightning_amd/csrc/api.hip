@@ -80,11 +80,13 @@ dsa_status check_batch(const dsa_batch* b, Batch* out) {
     return DSA_OK;
 }
 
-// Split count of the sparse MQA for a batch of T rows: enough workgroups to cover the chip
-// when there are few rows (decode), at least 128 selected slots per split.
+// Split count of the sparse MQA for a batch of T rows: about one workgroup per CU (256,
+// two workgroups of 64 heads per row) when there are few rows (decode), at least 128
+// selected slots per split.  More splits would run in a second round of workgroups and
+// write more partials.
 int mqa_splits(int T, int topk) {
     if (T <= 0 || T >= 128) return 1;
-    int n = (256 + T - 1) / T;
+    int n = (128 + T - 1) / T;
     const int cap = (topk + 127) / 128;
     if (n > cap) n = cap;
     if (n > 8) n = 8;

@@ -318,9 +318,10 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
 }
 
 constexpr int kDecodeThreads = 256;
-constexpr int kDecodeKeysPerWave = 512;
+constexpr int kDecodeKeysPerWave = 256;
 constexpr int kDecodeKeys = kDecodeKeysPerWave * (kDecodeThreads / kWave);
-constexpr int kDecodeUnroll = 4;
+constexpr int kDecodeUnroll = 4;  // 16-key groups per step (two steps in flight)
+static_assert(kDecodeUnroll % 4 == 0, "each lane group stores every fourth group");
 
 // Decode: one query row per sequence against its whole key cache.  The work is a stream of
 // 132 bytes per cached key, so each wave reads its key fragments straight from memory into
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kDecodeThreads) void indexer_decode_kernel(
     const int s_end = min(s_begin + kDecodeKeysPerWave, nkeys);
 
     v8i qa[NMT];
-    float wt[NMT][4];
+    float wt[NMT][4];  // half the folded weight: w * ReLU(x) = wt * x + wt * |x|
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
         const int h = mt * 16 + col;
@@ -361,43 +362,63 @@ __global__ __launch_bounds__(kDecodeThreads) void indexer_decode_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int hh = mt * 16 + grp * 4 + r;
-            wt[mt][r] = hh < H ? w[(int64_t)qrow * H + hh] * qs[(int64_t)qrow * H + hh] : 0.f;
+            wt[mt][r] = hh < H ? 0.5f * w[(int64_t)qrow * H + hh] * qs[(int64_t)qrow * H + hh] : 0.f;
         }
     }
     float* srow = scores + (int64_t)qrow * stride;
-    for (int s0 = s_begin; s0 < s_end; s0 += 16 * kDecodeUnroll) {
-        v8i bf[kDecodeUnroll];
-        float kscale[kDecodeUnroll];
+    // Key fragments of kDecodeUnroll 16-key groups per step, loaded one step ahead: the loads
+    // of step i+1 go out before the scores of step i are stored, so waiting for them never
+    // waits for those stores (stores and loads share one counter, which drains in order).
+    // Addresses are clamped to the wave's range (stores of clamped keys are masked), so the
+    // loads carry no branches.
+    struct Frag {
+        v8i b[kDecodeUnroll];
+        float ks[kDecodeUnroll];
+    };
+    auto load = [&](int s0, Frag& f) {
 #pragma unroll
         for (int u = 0; u < kDecodeUnroll; ++u) {
-            const int s = s0 + 16 * u + col;
-            v8i bv = {0, 0, 0, 0, 0, 0, 0, 0};
-            float sc = 0.f;
-            if (s < s_end) {
-                if (grp < KGRP) {
-                    const uint8_t* src = k8 + (int64_t)(kbase + s) * D + grp * 32;
-                    const v4i lo = *(const v4i*)src;
-                    const v4i hi = *(const v4i*)(src + 16);
-                    bv = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                }
-                sc = ks[kbase + s];
-            }
-            bf[u] = bv;
-            kscale[u] = sc;
+            const int s = min(s0 + 16 * u + col, s_end - 1);
+            const uint8_t* src = k8 + (int64_t)(kbase + s) * D + (grp < KGRP ? grp : 0) * 32;
+            const v4i lo = *(const v4i*)src;
+            const v4i hi = *(const v4i*)(src + 16);
+            f.b[u] = grp < KGRP ? (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}
+                                : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+            f.ks[u] = ks[kbase + s];
         }
+    };
+    constexpr int STEP = 16 * kDecodeUnroll;
+    constexpr int NSTEP = kDecodeKeysPerWave / STEP;
+    static_assert(kDecodeKeysPerWave % STEP == 0 && kDecodeUnroll == 4, "one score per lane and step");
+    // the wave's scores are held (one per lane and step) and stored after the loop, so no
+    // store is in flight while the key loads stream
+    float held[NSTEP];
+    Frag cur, nxt;
+    load(s_begin, nxt);
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+        const int s0 = s_begin + st * STEP;
+        cur = nxt;
+        if (st + 1 < NSTEP && s0 + STEP < s_end) load(s0 + STEP, nxt);
+        float sc[kDecodeUnroll];
 #pragma unroll
         for (int u = 0; u < kDecodeUnroll; ++u) {
             float part = 0.f;
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
-                const v4f acc = mfma_fp8_16x16x128(qa[mt], bf[u]);
+                const v4f acc = mfma_fp8_16x16x128(qa[mt], cur.b[u]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) part += wt[mt][r] * fmaxf(acc[r], 0.f);
+                for (int r = 0; r < 4; ++r) part = fmaf(wt[mt][r], fabsf(acc[r]), fmaf(wt[mt][r], acc[r], part));
             }
-            part = sum_over_groups(part);
-            const int s = s0 + 16 * u + col;
-            if (grp == 0 && s < s_end) srow[s] = part * kscale[u];
+            sc[u] = sum_over_groups(part) * cur.ks[u];  // every lane group holds the sum
         }
+        // lane group g keeps group u = g: 64 consecutive keys per step over all lanes
+        held[st] = grp == 0 ? sc[0] : grp == 1 ? sc[1] : grp == 2 ? sc[2] : sc[3];
+    }
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+        const int s = s_begin + st * STEP + 16 * grp + col;
+        if (s < s_end) srow[s] = held[st];
     }
 }
 
