@@ -288,7 +288,9 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
     const int64_t stride = score_stride_for(bt);
     // the idx area is reserved even when idx_out is given (plan_forward's layout)
     auto bytes_for = [&](int c) { return plan_forward(dims, shape, bt, c).total; };
-    const size_t per_row = (size_t)stride * sizeof(float) + (size_t)topk * 4 + topk_ws_bytes(1, bt.max_lk, topk);
+    // first estimate from the per-row areas (top-k candidates are only kept for passes of
+    // fewer than 128 rows); bytes_for then gives the exact size
+    const size_t per_row = (size_t)stride * sizeof(float) + (size_t)topk * 4;
     int64_t c64 = (int64_t)(ws_bytes / per_row);
     int chunk = (int)(c64 < bt.max_lq ? c64 : bt.max_lq);
     if (chunk > kRowGranule) chunk -= chunk % kRowGranule;
