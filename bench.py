@@ -10,7 +10,9 @@ Besides the end-to-end rate the line carries:
                 same row passes as dsa_forward makes), measured with HIP events on the stream
                 the kernels run on, and each stage's algorithmic rate;
   roofline      the dominant stage's achieved rate against its MI355X peak;
-  decode        batched decode (32 sequences, lengths uniform in [32768, 131072]);
+  decode        batched decode (32 sequences, lengths uniform in [32768, 131072]): the
+                forward step, the cache producer (RoPE + FP8 codes of the new tokens, cache
+                append) alone, and both together;
   cpu_baseline  the CPU oracle on a bounded, uniformly spaced sample of query rows of the
                 same workload, timed on the host (rank 0 only).
 """
@@ -184,20 +186,42 @@ def decode_case(dev, steps):
     lse = torch.empty(B, dims.n_heads, dtype=torch.float32, device=dev)
     ws = torch.empty(dsa.workspace_size(dims, batch), dtype=torch.uint8, device=dev)
 
+    # the cache producer of the step: the new tokens' indexer query and key (before RoPE and
+    # quantisation) and latent rows, rotary tables for every position
+    g = torch.Generator(device=dev).manual_seed(1)
+    q_idx = torch.randn(B, dims.n_idx_heads, dims.idx_dim, generator=g, device=dev)
+    k_idx = torch.randn(B, dims.idx_dim, generator=g, device=dev)
+    kv_new = torch.randn(B, dims.qk_dim, generator=g, device=dev).to(torch.bfloat16)
+    n_pos = max(inp["lens"])
+    rd = dims.idx_dim // 2
+    ang = torch.arange(n_pos, dtype=torch.float64)[:, None] * \
+        10000.0 ** (-2.0 * torch.arange(rd // 2, dtype=torch.float64) / rd)[None, :]
+    cos, sin = ang.cos().float().to(dev), ang.sin().float().to(dev)
+
+    def append():
+        dsa.cache_append(dims, batch, q_idx, k_idx, kv_new, cos, sin, inp["q8"], inp["q_scale"],
+                         inp["k8"], inp["k_scale"], inp["kv"])
+
     def step():
         dsa.forward(dims, batch, inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"],
                     inp["q"], inp["kv"], out, lse, None, ws)
 
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    with Timer() as tm:
-        for _ in range(steps):
-            step()
-    us = tm.ms() * 1e3 / steps
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        with Timer() as tm:
+            for _ in range(steps):
+                fn()
+        return tm.ms() * 1e3 / steps
+
+    us_app = timed(append)
+    us = timed(step)
+    us_all = timed(lambda: (append(), step()))
     nkeys = int(inp["cu_k"][-1])
     return dict(us_per_step=round(us, 2), us_per_token=round(us / B, 3), batch=B,
-                mean_context=round(nkeys / B), hbm_floor_mb=round((nkeys * 132 + B * 2048 * 1152) / 1e6, 1))
+                mean_context=round(nkeys / B), hbm_floor_mb=round((nkeys * 132 + B * 2048 * 1152) / 1e6, 1),
+                cache_append_us=round(us_app, 2), us_per_step_with_append=round(us_all, 2))
 
 
 def cpu_baseline(c, budget_s=20.0, max_rows=192):

@@ -63,13 +63,24 @@ typedef struct {
     float sm_scale;      /* softmax scale applied to q.c (1/sqrt(192))               */
 } dsa_dims;
 
-/* Sequence layout of a batch.  The host and device arrays must hold the same values. */
+/* Sequence layout of a batch.  The host and device arrays must hold the same values.
+ * Caches (k8, k_scale, kv) are packed by default: sequence b's positions 0 .. len_k-1 are
+ * rows cu_k[b] .. cu_k[b+1]-1.  With page_table_dev set they are paged instead, in pages
+ * of DSA_PAGE_SIZE positions (the serving setups on the DeepSeek-V3.2-Exp pages use page
+ * size 64): position p of sequence b is cache row
+ *     page_table_dev[b * pages_per_seq + p / 64] * 64 + p % 64
+ * of the caller's page pool (page ids trusted like indices; a row offset in bytes must fit in
+ * 32 bits).  Paged caches are read by the decode paths (every sequence with one query row),
+ * dsa_sparse_mqa and dsa_cache_append; prefill with paged caches returns DSA_ERR_UNSUPPORTED. */
+#define DSA_PAGE_SIZE 64
 typedef struct {
-    int32_t n_seqs;           /* B >= 1                                               */
-    const int32_t* cu_q_host; /* [B+1] query row offsets, host memory, cu_q[0] = 0    */
-    const int32_t* cu_k_host; /* [B+1] key row offsets, host memory, cu_k[0] = 0      */
-    const int32_t* cu_q_dev;  /* [B+1] the same offsets in device memory              */
-    const int32_t* cu_k_dev;  /* [B+1]                                                */
+    int32_t n_seqs;                 /* B >= 1                                          */
+    const int32_t* cu_q_host;       /* [B+1] query row offsets, host memory, cu_q[0] = 0 */
+    const int32_t* cu_k_host;       /* [B+1] key row offsets, host memory, cu_k[0] = 0   */
+    const int32_t* cu_q_dev;        /* [B+1] the same offsets in device memory         */
+    const int32_t* cu_k_dev;        /* [B+1]                                           */
+    const int32_t* page_table_dev;  /* [B, pages_per_seq] page ids, or NULL (packed)    */
+    int32_t pages_per_seq;          /* >= ceil(max len_k / 64) when paged               */
 } dsa_batch;
 
 /* Bytes of workspace that dsa_forward (and dsa_sparse_mqa, which needs less) uses by
@@ -141,6 +152,29 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
                        const float* k_scale, const uint16_t* q, const uint16_t* kv,
                        uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/* Decode cache producer (the indexer's RoPE + FP8 step before the selection: DeepSeek-V3.2-Exp
+ * lightning-indexer walk-through, step 2 — rotary encoding of the first 64 dims of the indexer
+ * query and key, FP8 quantisation of both, the key codes and their scale kept in the cache).
+ * For the len_q new tokens of each sequence (positions len_k - len_q + i, already counted in
+ * cu_k):
+ *   - RoPE on dims 0 .. R-1 (R = idx_dim / 2: 64 for the production shape): pairs (2i, 2i+1)
+ *     rotate by the caller's table angle for (position, i),
+ *         r0 = x0*cos - x1*sin,  r1 = x0*sin + x1*cos   (float32, each product and sum rounded);
+ *   - per row (each query head, and the key) scale = amax/448 (1 for an all-zero row) and
+ *     e4m3fn codes of x/scale (round to nearest even, clamped to +-448), all in float32;
+ *   - the key's codes and scale are written to the caches at the token's cache row (packed or
+ *     paged, see dsa_batch), and the token's bf16 latent row is copied there when given.
+ *   q_idx  [T, n_idx_heads, idx_dim] float32,  k_idx [T, idx_dim] float32  (before RoPE)
+ *   kv_new [T, qk_dim] bf16 bits or NULL (then kv_cache may be NULL)
+ *   rope_cos, rope_sin [n_pos, R/2] float32, n_pos > every new token's position
+ *   q8 [T, n_idx_heads, idx_dim] uint8 and q_scale [T, n_idx_heads] float32 receive the
+ *   query codes; k8_cache [rows, idx_dim], k_scale_cache [rows], kv_cache [rows, qk_dim]. */
+dsa_status dsa_cache_append(const dsa_dims* dims, const dsa_batch* batch, const float* q_idx,
+                            const float* k_idx, const uint16_t* kv_new, const float* rope_cos,
+                            const float* rope_sin, int32_t n_pos, uint8_t* q8, float* q_scale,
+                            uint8_t* k8_cache, float* k_scale_cache, uint16_t* kv_cache,
+                            hipStream_t stream);
 
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status status);

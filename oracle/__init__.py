@@ -213,3 +213,88 @@ def forward_rows(inp: dict, rows, seq: int = 0):
     out, lse = sparse_mqa(np.asarray(inp["q"])[qr], np.asarray(inp["kv"])[k0:k1], idx,
                           dims.v_dim, dims.sm_scale)
     return dict(scores=scores, idx=idx, out=out, lse=lse, pos=pos)
+
+
+# ---- cache producer: RoPE, FP8 quantisation, cache append ---------------------------------
+# (DeepSeek-V3.2-Exp lightning-indexer walk-through, step 2: rotary position encoding of the
+# first 64 dims of the indexer query and key, then FP8 quantisation of both with the key
+# codes and their scale kept in the cache.)  The rotation and the quantiser are evaluated in
+# float32 with every product, sum and quotient rounded separately, the precision in which the
+# GPU path decides each FP8 code, so both sides make the same rounding decisions.
+
+_E4M3_VALUES = None
+
+
+def _e4m3_table():
+    """(finite values ascending, their codes) of the e4m3fn format: 1 sign, 4 exponent
+    (bias 7), 3 mantissa bits; exponent 0 is subnormal (m * 2^-9); code 0x7f/0xff are NaN."""
+    global _E4M3_VALUES
+    if _E4M3_VALUES is None:
+        codes = [c for c in range(256) if (c & 0x7f) != 0x7f and c != 0x80]  # -0 folded into +0
+        vals = decode_e4m3(np.array(codes, np.uint8))
+        order = np.argsort(vals, kind="stable")
+        _E4M3_VALUES = (vals[order], np.array(codes, np.uint8)[order])
+    return _E4M3_VALUES
+
+
+def encode_e4m3(x) -> np.ndarray:
+    """Round each value to the nearest e4m3fn value, ties to the even code (mantissa bit 0
+    clear), saturating at +-448 (the format has no infinity).  -0 and values that round to
+    zero from below give code 0x80; NaN gives 0x7f.  Brute force over the 254 finite values."""
+    vals, codes = _e4m3_table()
+    x = np.asarray(x, np.float64)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+    for i, v in enumerate(flat):
+        if np.isnan(v):
+            out[i] = 0x7F
+            continue
+        a = min(abs(v), 448.0)
+        d = np.abs(vals - a)
+        best = np.flatnonzero(d == d.min())
+        c = codes[best[0]]
+        if len(best) > 1:  # a tie between two neighbours: the even mantissa wins
+            even = [b for b in best if (codes[b] & 1) == 0]
+            c = codes[even[0]]
+        if np.signbit(v):
+            c = c | 0x80
+        out[i] = c
+    return out.reshape(x.shape)
+
+
+def rope_f32(x, pos, cos_tab, sin_tab, rope_dim: int):
+    """Rotary encoding of the first rope_dim dims of x[..., d] (float32) at position pos:
+    pairs (2i, 2i+1) rotate by the table's angle for (pos, i),
+        r0 = x0*c - x1*s,  r1 = x0*s + x1*c,
+    each product and sum rounded to float32; the other dims pass unchanged."""
+    x = np.array(x, np.float32, copy=True)
+    c = np.float32(cos_tab[pos, : rope_dim // 2])
+    s = np.float32(sin_tab[pos, : rope_dim // 2])
+    x0 = x[..., 0:rope_dim:2].copy()
+    x1 = x[..., 1:rope_dim:2].copy()
+    r0 = np.float32(np.float32(x0 * c) - np.float32(x1 * s))
+    r1 = np.float32(np.float32(x0 * s) + np.float32(x1 * c))
+    x[..., 0:rope_dim:2] = r0
+    x[..., 1:rope_dim:2] = r1
+    return x
+
+
+def quantize_row_e4m3(x):
+    """One scale per row of x[..., d] (float32): amax/448 (1 for an all-zero row), codes of
+    x / scale clamped to +-448, all in float32."""
+    x = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, np.float32(amax / np.float32(448.0)), np.float32(1.0)).astype(np.float32)
+    y = np.clip(np.float32(x / scale[..., None]), np.float32(-448.0), np.float32(448.0))
+    return encode_e4m3(y), scale
+
+
+def cache_append(q_idx, k_idx, pos, cos_tab, sin_tab, rope_dim: int):
+    """New tokens' indexer entries: q_idx [n, H, d] and k_idx [n, d] float32 at positions
+    pos[n] -> (q8 [n, H, d], q_scale [n, H], k8 [n, d], k_scale [n])."""
+    q8, qs, k8, ks = [], [], [], []
+    for i, p in enumerate(pos):
+        a, sa = quantize_row_e4m3(rope_f32(q_idx[i], p, cos_tab, sin_tab, rope_dim))
+        b, sb = quantize_row_e4m3(rope_f32(k_idx[i], p, cos_tab, sin_tab, rope_dim))
+        q8.append(a); qs.append(sa); k8.append(b); ks.append(sb)
+    return np.stack(q8), np.stack(qs), np.stack(k8), np.array(ks, np.float32)

@@ -49,21 +49,37 @@ class Dims(ctypes.Structure):
 class _CBatch(ctypes.Structure):
     _fields_ = [("n_seqs", ctypes.c_int32), ("cu_q_host", ctypes.c_void_p),
                 ("cu_k_host", ctypes.c_void_p), ("cu_q_dev", ctypes.c_void_p),
-                ("cu_k_dev", ctypes.c_void_p)]
+                ("cu_k_dev", ctypes.c_void_p), ("page_table_dev", ctypes.c_void_p),
+                ("pages_per_seq", ctypes.c_int32)]
+
+
+PAGE_SIZE = 64  # positions per cache page (DSA_PAGE_SIZE)
 
 
 class Batch:
-    """Sequence offsets in host and device memory, kept alive together."""
+    """Sequence offsets in host and device memory, kept alive together.
 
-    def __init__(self, cu_q, cu_k, device="cuda"):
+    page_table: optional int32 array [B, pages_per_seq] of page ids; the caches are then paged
+    (position p of sequence b is cache row page_table[b, p // 64] * 64 + p % 64)."""
+
+    def __init__(self, cu_q, cu_k, device="cuda", page_table=None):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int32))
         self.cu_k = np.ascontiguousarray(np.asarray(cu_k, dtype=np.int32))
         if self.cu_q.shape != self.cu_k.shape or self.cu_q.ndim != 1 or len(self.cu_q) < 2:
             raise ValueError("cu_q and cu_k must be 1-D with the same length >= 2")
         self.cu_q_dev = torch.from_numpy(self.cu_q).to(device)
         self.cu_k_dev = torch.from_numpy(self.cu_k).to(device)
+        self.page_table_dev = None
+        pps = 0
+        if page_table is not None:
+            pt = torch.as_tensor(page_table, dtype=torch.int32)
+            if pt.ndim != 2 or pt.shape[0] != len(self.cu_q) - 1:
+                raise ValueError("page_table must be [n_seqs, pages_per_seq]")
+            self.page_table_dev = pt.contiguous().to(device)
+            pps = int(pt.shape[1])
         self.c = _CBatch(len(self.cu_q) - 1, self.cu_q.ctypes.data, self.cu_k.ctypes.data,
-                         self.cu_q_dev.data_ptr(), self.cu_k_dev.data_ptr())
+                         self.cu_q_dev.data_ptr(), self.cu_k_dev.data_ptr(),
+                         None if self.page_table_dev is None else self.page_table_dev.data_ptr(), pps)
 
     @property
     def n_seqs(self) -> int:
@@ -104,6 +120,7 @@ def lib():
             "dsa_topk_workspace_size": [P, P, P],
             "dsa_sparse_mqa": [P, P, P, P, P, P, P, P, S, P],
             "dsa_forward": [P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
+            "dsa_cache_append": [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P],
         }.items():
             fn = getattr(L, name)
             fn.argtypes = args
@@ -199,3 +216,15 @@ def forward(dims, batch: Batch, q8, q_scale, w, k8, k_scale, q, kv, out, lse=Non
 
 PROD_DIMS = Dims(64, 128, 2048, 128, 576, 512, 1.0 / np.sqrt(192.0))
 TINY_DIMS = Dims(4, 32, 32, 8, 80, 64, 1.0 / np.sqrt(80.0))
+
+
+def cache_append(dims, batch: Batch, q_idx, k_idx, kv_new, rope_cos, rope_sin, q8, q_scale,
+                 k8_cache, k_scale_cache, kv_cache=None, stream=None):
+    """RoPE + FP8 codes of the new tokens' indexer query and key; the key codes, scale and
+    (if kv_new is given) latent row are written at each new token's cache row."""
+    d = _dims(dims)
+    _check(lib().dsa_cache_append(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q_idx), _ptr(k_idx),
+                                  _ptr(kv_new), _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.shape[0]),
+                                  _ptr(q8), _ptr(q_scale), _ptr(k8_cache), _ptr(k_scale_cache),
+                                  _ptr(kv_cache), _stream(stream)), "dsa_cache_append")
+    return q8, q_scale

@@ -27,6 +27,8 @@ struct Batch {
     int max_lk = 0;
     int max_lq = 0;
     bool decode = false;  // every sequence has exactly one query row
+    const int32_t* pages = nullptr;  // paged caches (device page table) or nullptr
+    int pages_per_seq = 0;
     const dsa_batch* raw = nullptr;
     int lq(int b) const { return raw->cu_q_host[b + 1] - raw->cu_q_host[b]; }
     int lk(int b) const { return raw->cu_k_host[b + 1] - raw->cu_k_host[b]; }
@@ -76,6 +78,11 @@ dsa_status check_batch(const dsa_batch* b, Batch* out) {
     }
     r.T = b->cu_q_host[b->n_seqs];
     r.S = b->cu_k_host[b->n_seqs];
+    if (b->page_table_dev != nullptr) {
+        if (b->pages_per_seq < 1 || (int64_t)b->pages_per_seq * kPage < r.max_lk) return DSA_ERR_INVALID_ARG;
+        r.pages = b->page_table_dev;
+        r.pages_per_seq = b->pages_per_seq;
+    }
     *out = r;
     return DSA_OK;
 }
@@ -150,7 +157,9 @@ dsa_status dsa_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size
     if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
     if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
     const ForwardPlan p = plan_forward(dims, shape, bt, default_chunk(bt));
-    *bytes = p.total;
+    // dsa_sparse_mqa on the whole batch splits fewer than 128 rows over several workgroups
+    const size_t mqa = align_up(mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, dims->topk)));
+    *bytes = p.total > mqa ? p.total : mqa;
     return DSA_OK;
 }
 
@@ -184,7 +193,9 @@ dsa_status dsa_indexer_scores(const dsa_dims* dims, const dsa_batch* batch, cons
     if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
     IndexerArgs a{shape, q8, q_scale, w, k8, k_scale, scores, score_stride};
     if (bt.decode)
-        return hip_status(launch_indexer_decode(a, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, stream));
+        return hip_status(launch_indexer_decode(a, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, bt.pages,
+                                                bt.pages_per_seq, stream));
+    if (bt.pages != nullptr) return DSA_ERR_UNSUPPORTED;  // paged caches: decode batches only
     for (int b = 0; b < bt.B; ++b) {
         const int lq = bt.lq(b), lk = bt.lk(b);
         if (lq == 0) continue;
@@ -218,7 +229,7 @@ dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* s
     if (!scores || !idx || !aligned16(scores) || !aligned16(idx)) return DSA_ERR_INVALID_ARG;
     if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
     if (ws != nullptr && !aligned16(ws)) return DSA_ERR_WORKSPACE;
-    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
+    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
     return hip_status(launch_topk(scores, score_stride, idx, dims->topk, map, bt.T, bt.max_lk, ws,
                                   ws == nullptr ? 0 : ws_bytes, stream));
 }
@@ -240,7 +251,7 @@ dsa_status dsa_sparse_mqa(const dsa_dims* dims, const dsa_batch* batch, const ui
     const size_t need = mqa_split_bytes(shape, bt.T, n_split);
     if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return DSA_ERR_WORKSPACE;
     MqaArgs a{shape, q, kv, idx, dims->topk, out, lse, dims->sm_scale};
-    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
+    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
     return hip_status(launch_sparse_mqa(a, map, bt.T, n_split, ws, stream));
 }
 
@@ -271,13 +282,14 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
         float* sc = (float*)(wsb + p.scores_off);
         int32_t* ix = idx_out ? idx_out : (int32_t*)(wsb + p.idx_off);
         IndexerArgs ia{shape, q8, q_scale, w, k8, k_scale, sc, p.stride};
-        RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
+        RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
         const int n_split = mqa_splits(bt.T, topk);
         MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale};
         if (debug_log())
             fprintf(stderr, "[dsa] decode B=%d max_len_k=%d stride=%lld splits=%d\n", bt.B, bt.max_lk,
                     (long long)p.stride, n_split);
-        hipError_t e = launch_indexer_decode(ia, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, stream);
+        hipError_t e = launch_indexer_decode(ia, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, bt.pages,
+                                             bt.pages_per_seq, stream);
         if (e == hipSuccess)
             e = launch_topk(sc, p.stride, ix, topk, map, bt.T, bt.max_lk, wsb + p.tail_off, p.topk_bytes, stream);
         if (e == hipSuccess) e = launch_sparse_mqa(ma, map, bt.T, n_split, wsb + p.tail_off, stream);
@@ -285,6 +297,7 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
     }
 
     // Prefill: passes of `chunk` query rows per sequence.
+    if (bt.pages != nullptr) return DSA_ERR_UNSUPPORTED;  // paged caches: decode batches only
     const int64_t stride = score_stride_for(bt);
     // the idx area is reserved even when idx_out is given (plan_forward's layout)
     auto bytes_for = [&](int c) { return plan_forward(dims, shape, bt, c).total; };
@@ -328,6 +341,30 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
         }
     }
     return DSA_OK;
+}
+
+dsa_status dsa_cache_append(const dsa_dims* dims, const dsa_batch* batch, const float* q_idx,
+                            const float* k_idx, const uint16_t* kv_new, const float* rope_cos,
+                            const float* rope_sin, int32_t n_pos, uint8_t* q8, float* q_scale,
+                            uint8_t* k8_cache, float* k_scale_cache, uint16_t* kv_cache,
+                            hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!q_idx || !k_idx || !rope_cos || !rope_sin || !q8 || !q_scale || !k8_cache || !k_scale_cache)
+        return DSA_ERR_INVALID_ARG;
+    if ((kv_new == nullptr) != (kv_cache == nullptr)) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(rope_cos) || !aligned16(rope_sin) ||
+        !aligned16(q8) || !aligned16(q_scale) || !aligned16(k8_cache) || !aligned16(k_scale_cache) ||
+        (kv_new != nullptr && (!aligned16(kv_new) || !aligned16(kv_cache))))
+        return DSA_ERR_INVALID_ARG;
+    if (n_pos < bt.max_lk) return DSA_ERR_INVALID_ARG;  // every new position has a table row
+    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
+    CacheAppendArgs a{shape, q_idx, k_idx, kv_new, rope_cos, rope_sin, q8, q_scale, k8_cache, k_scale_cache, kv_cache};
+    return hip_status(launch_cache_append(a, map, bt.T, stream));
 }
 
 }  // extern "C"

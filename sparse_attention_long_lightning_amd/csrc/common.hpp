@@ -21,6 +21,8 @@ constexpr int kMaxTopk = 2048;
 //  single-sequence mode (cu_q == nullptr): row i -> position pos0 + i, key base kbase,
 //      query row row0 + i of the packed query arrays;
 //  batch mode: row i is a global query row; its sequence b is found in cu_q.
+//  paged caches (pages != nullptr): position p of sequence s is cache row
+//      pages[s * pages_per_seq + p / kPage] * kPage + p % kPage.
 struct RowMap {
     const int32_t* cu_q;
     const int32_t* cu_k;
@@ -28,13 +30,24 @@ struct RowMap {
     int row0;
     int pos0;
     int kbase;
+    const int32_t* pages = nullptr;
+    int pages_per_seq = 0;
 };
+
+constexpr int kPage = 64;  // positions per cache page
 
 struct RowInfo {
     int qrow;   // packed query row
     int pos;    // absolute position p (keys 0..p)
     int kbase;  // packed key row of position 0
+    int seq;    // sequence of the row
 };
+
+// Cache row of position p of the row's sequence.
+__device__ __forceinline__ int64_t cache_row(const RowMap& m, const RowInfo& r, int p) {
+    if (m.pages == nullptr) return (int64_t)r.kbase + p;
+    return (int64_t)m.pages[(int64_t)r.seq * m.pages_per_seq + p / kPage] * kPage + p % kPage;
+}
 
 __device__ __forceinline__ RowInfo row_info(const RowMap& m, int i) {
     RowInfo r;
@@ -42,6 +55,7 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& m, int i) {
         r.qrow = m.row0 + i;
         r.pos = m.pos0 + i;
         r.kbase = m.kbase;
+        r.seq = 0;
         return r;
     }
     int lo = 0, hi = m.n_seqs - 1;  // last b with cu_q[b] <= i
@@ -55,6 +69,7 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& m, int i) {
     r.qrow = i;
     r.pos = lk - lq + (i - m.cu_q[b]);
     r.kbase = m.cu_k[b];
+    r.seq = b;
     return r;
 }
 

@@ -330,7 +330,8 @@ template <int H, int D>
 __global__ __launch_bounds__(kDecodeThreads) void indexer_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, float* __restrict__ scores,
-    int64_t stride, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k) {
+    int64_t stride, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    const int32_t* __restrict__ pages, int pages_per_seq) {
     constexpr int NMT = (H + 15) / 16;
     constexpr int KGRP = D / 32;
     const int tid = threadIdx.x;
@@ -375,16 +376,24 @@ __global__ __launch_bounds__(kDecodeThreads) void indexer_decode_kernel(
         v8i b[kDecodeUnroll];
         float ks[kDecodeUnroll];
     };
+    // Cache row of the step's first key: a step of 64 keys is one page of a paged cache
+    // (steps start at multiples of 64).
+    static_assert(16 * kDecodeUnroll == kPage && kDecodeKeysPerWave % kPage == 0, "one page per step");
+    auto step_row = [&](int s0) -> int64_t {
+        if (pages == nullptr) return (int64_t)kbase + s0;
+        return (int64_t)pages[(int64_t)b * pages_per_seq + s0 / kPage] * kPage;
+    };
     auto load = [&](int s0, Frag& f) {
+        const int64_t r0 = step_row(s0);
 #pragma unroll
         for (int u = 0; u < kDecodeUnroll; ++u) {
-            const int s = min(s0 + 16 * u + col, s_end - 1);
-            const uint8_t* src = k8 + (int64_t)(kbase + s) * D + (grp < KGRP ? grp : 0) * 32;
+            const int ds = min(s0 + 16 * u + col, s_end - 1) - s0;
+            const uint8_t* src = k8 + (r0 + ds) * D + (grp < KGRP ? grp : 0) * 32;
             const v4i lo = *(const v4i*)src;
             const v4i hi = *(const v4i*)(src + 16);
             f.b[u] = grp < KGRP ? (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}
                                 : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-            f.ks[u] = ks[kbase + s];
+            f.ks[u] = ks[r0 + ds];
         }
     };
     constexpr int STEP = 16 * kDecodeUnroll;
@@ -436,10 +445,11 @@ hipError_t launch_prefill_t(const IndexerArgs& a, int row0, int n_rows, int pos0
 
 template <int H, int D>
 hipError_t launch_decode_t(const IndexerArgs& a, int n_seqs, int max_keys, const int32_t* cu_q,
-                           const int32_t* cu_k, hipStream_t st) {
+                           const int32_t* cu_k, const int32_t* pages, int pages_per_seq, hipStream_t st) {
     dim3 grid((max_keys + kDecodeKeys - 1) / kDecodeKeys, n_seqs);
     hipLaunchKernelGGL((indexer_decode_kernel<H, D>), grid, dim3(kDecodeThreads), 0, st, a.q8,
-                       a.q_scale, a.w, a.k8, a.k_scale, a.scores, a.score_stride, cu_q, cu_k);
+                       a.q_scale, a.w, a.k8, a.k_scale, a.scores, a.score_stride, cu_q, cu_k, pages,
+                       pages_per_seq);
     return hipGetLastError();
 }
 
@@ -452,9 +462,11 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a, int row0, int n_rows, in
 }
 
 hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,
-                                 const int32_t* cu_q, const int32_t* cu_k, hipStream_t st) {
-    if (a.shape == Shape::Prod) return launch_decode_t<64, 128>(a, n_seqs, max_keys, cu_q, cu_k, st);
-    return launch_decode_t<4, 32>(a, n_seqs, max_keys, cu_q, cu_k, st);
+                                 const int32_t* cu_q, const int32_t* cu_k, const int32_t* pages,
+                                 int pages_per_seq, hipStream_t st) {
+    if (a.shape == Shape::Prod)
+        return launch_decode_t<64, 128>(a, n_seqs, max_keys, cu_q, cu_k, pages, pages_per_seq, st);
+    return launch_decode_t<4, 32>(a, n_seqs, max_keys, cu_q, cu_k, pages, pages_per_seq, st);
 }
 
 }  // namespace dsa

@@ -27,8 +27,10 @@ struct IndexerArgs {
 hipError_t launch_indexer_prefill(const IndexerArgs& a, int row0, int n_rows, int pos0,
                                   int kbase, float* scores, hipStream_t st);
 // Decode: one query row per sequence (cu_q[b+1] - cu_q[b] == 1); row cu_q[b] of the scores.
+// Paged caches: pages != nullptr (see RowMap).
 hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,
-                                 const int32_t* cu_q, const int32_t* cu_k, hipStream_t st);
+                                 const int32_t* cu_q, const int32_t* cu_k, const int32_t* pages,
+                                 int pages_per_seq, hipStream_t st);
 
 // Top-k over n_rows score rows; row i reads scores + i * stride and writes idx + i * topk.
 // With a workspace of topk_ws_bytes(n_rows, max_len, topk) bytes (max_len = the longest
@@ -56,5 +58,23 @@ size_t mqa_split_bytes(Shape shape, int n_rows, int n_split);
 // merges the partials (ws must hold mqa_split_bytes).
 hipError_t launch_sparse_mqa(const MqaArgs& a, const RowMap& map, int n_rows, int n_split,
                              void* ws, hipStream_t st);
+
+struct CacheAppendArgs {
+    Shape shape;
+    const float* q_idx;      // [T, H_I, d_I] new tokens' indexer queries (before RoPE)
+    const float* k_idx;      // [T, d_I] new tokens' indexer keys (before RoPE)
+    const uint16_t* kv_new;  // [T, qk_dim] bf16 latent rows, or nullptr
+    const float* rope_cos;   // [n_pos, d_I / 4]
+    const float* rope_sin;
+    uint8_t* q8;             // [T, H_I, d_I]
+    float* q_scale;          // [T, H_I]
+    uint8_t* k8_cache;       // rows of the caches (packed or paged, see RowMap)
+    float* k_scale_cache;
+    uint16_t* kv_cache;
+};
+
+// RoPE + FP8 codes of the new tokens' indexer query and key; key codes, scale and latent row
+// written at each token's cache row.
+hipError_t launch_cache_append(const CacheAppendArgs& a, const RowMap& map, int n_rows, hipStream_t st);
 
 }  // namespace dsa

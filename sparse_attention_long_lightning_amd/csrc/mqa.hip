@@ -257,17 +257,21 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     const int j1 = min(topk, j0 + per);
     const int nblk = j1 > j0 ? (j1 - j0 + kBlk - 1) / kBlk : 0;
     const int32_t* irow = idx + (int64_t)row * topk;
-    const uint8_t* kvb = (const uint8_t*)(kv + (int64_t)ri.kbase * DQK);
+    // latent rows are addressed from the sequence's first row (packed caches) or from the
+    // start of the page pool (paged caches)
+    const bool paged = map.pages != nullptr;
+    const uint8_t* kvb = (const uint8_t*)(paged ? kv : kv + (int64_t)ri.kbase * DQK);
     const int half = lane >> 5;
     const int mi = lane & 31;
     const int j16 = lane & 15;
     const uint32_t lds0 = lds_addr(lds);
 
-    // Row offsets (row 0 for an empty slot; a row's offset must fit in 31 bits) and occupancy
+    // Row offsets (row 0 for an empty slot; a row's offset must fit in 32 bits) and occupancy
     // of block b, staged in ring slot b % RING: the first RING blocks here, the rest by wave 0
     // one step before the loads need them.
     auto stage = [&](int b, int id) {  // lanes 0..31 hold the ids of the block's slots
-        if (lane < kBlk) rofs[b % C::RING][lane] = id >= 0 ? (uint32_t)id * (uint32_t)C::ROW_BYTES : 0u;
+        const uint32_t r = id < 0 ? 0u : paged ? (uint32_t)cache_row(map, ri, id) : (uint32_t)id;
+        if (lane < kBlk) rofs[b % C::RING][lane] = r * (uint32_t)C::ROW_BYTES;
         const uint64_t m = __ballot(id >= 0);
         if (lane == 0) rmask[b % C::RING] = (uint32_t)m;
     };

@@ -139,3 +139,55 @@ def test_topk_workspace_covers_the_segment_candidates():
     # workgroup per row: no workspace
     assert dsa.topk_workspace_size(d, cpu_batch([0, 1], [0, 8 * 16384 + 1])) == 0
     assert dsa.topk_workspace_size(d, cpu_batch([0, 128], [0, 5000])) == 0
+
+
+def call_append(dims, batch, ptr=FAKE, n_pos=1 << 20, **over):
+    args = dict(q_idx=ptr, k_idx=ptr, kv_new=ptr, cos=ptr, sin=ptr, q8=ptr, q_scale=ptr, k8=ptr,
+                k_scale=ptr, kv=ptr)
+    args.update(over)
+    return dsa.lib().dsa_cache_append(ctypes.byref(dims), ctypes.byref(batch.c), args["q_idx"],
+                                      args["k_idx"], args["kv_new"], args["cos"], args["sin"], n_pos,
+                                      args["q8"], args["q_scale"], args["k8"], args["k_scale"],
+                                      args["kv"], None)
+
+
+def test_cache_append_rejects_bad_arguments():
+    d, b = dims_with(), cpu_batch([0, 1, 2], [0, 100, 300])
+    for name in ("q_idx", "k_idx", "cos", "sin", "q8", "q_scale", "k8", "k_scale"):
+        assert call_append(d, b, **{name: None}) == INVALID, name
+        assert call_append(d, b, **{name: FAKE + 4}) == INVALID, name
+    assert call_append(d, b, kv_new=None) == INVALID       # latent row without a latent cache
+    assert call_append(d, b, kv=None) == INVALID
+    assert call_append(d, b, kv=FAKE + 2) == INVALID
+    assert call_append(d, b, n_pos=199) == INVALID          # no table row for position 199
+    assert call_append(dims_with(idx_dim=64), b) == UNSUPPORTED
+    assert call_append(d, cpu_batch([0, 0], [0, 5]), ptr=None) == OK  # nothing to append
+
+
+def test_paged_batches_are_validated():
+    d = dims_with()
+    pt = np.zeros((2, 4), np.int32)
+    dec = dsa.Batch([0, 1, 2], [0, 256, 356], device="cpu", page_table=pt)
+    assert dec.c.pages_per_seq == 4
+    short = dsa.Batch([0, 1, 2], [0, 257, 300], device="cpu", page_table=pt)  # 257 keys > 4 pages
+    assert call_forward(d, short) == INVALID
+    assert call_append(d, short) == INVALID
+    bad = dsa.Batch([0, 1, 2], [0, 256, 356], device="cpu", page_table=pt)
+    bad.c.pages_per_seq = 0
+    assert call_forward(d, bad) == INVALID
+    # prefill (a sequence with several query rows) reads packed caches only
+    pre = dsa.Batch([0, 2, 3], [0, 256, 356], device="cpu", page_table=pt)
+    assert call_forward(d, pre) == UNSUPPORTED
+    assert dsa.lib().dsa_indexer_scores(ctypes.byref(d), ctypes.byref(pre.c), FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, 256, None) == UNSUPPORTED
+    with pytest.raises(ValueError):
+        dsa.Batch([0, 1, 2], [0, 5, 6], device="cpu", page_table=np.zeros((3, 1), np.int32))
+
+
+def test_workspace_size_covers_the_attention_split_of_small_batches():
+    d = dims_with()
+    # 24 query rows of one sequence: dsa_sparse_mqa splits each row over several workgroups
+    b = cpu_batch([0, 24], [0, 5000])
+    need = dsa.workspace_size(d, b)
+    assert dsa.lib().dsa_sparse_mqa(ctypes.byref(d), ctypes.byref(b.c), FAKE, FAKE, FAKE, FAKE, None,
+                                    FAKE, need - 16, None) == WORKSPACE

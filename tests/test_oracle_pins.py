@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import dsa_inputs
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -352,3 +353,75 @@ def test_quantiser_round_trip():
     # round to nearest: error at most half a code step (relative 2^-4 for normal codes)
     err = (dec - x.double()).abs()
     assert torch.all(err <= x.double().abs() * 2.0 ** -4 + scale.double()[:, None] * 2.0 ** -10)
+
+
+# ---- cache producer: e4m3 encoder, RoPE, row quantiser ------------------------------------
+
+def test_encode_e4m3_round_trips_every_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    back = oracle.encode_e4m3(oracle.decode_e4m3(codes).astype(np.float32))
+    assert np.array_equal(back, codes)  # including -0 -> 0x80
+
+
+def test_encode_e4m3_ties_go_to_the_even_code_and_saturate():
+    codes = np.arange(0, 0x7E, dtype=np.uint8)  # non-negative finite codes, ascending values
+    vals = oracle.decode_e4m3(codes)
+    mid = (vals[:-1] + vals[1:]) / 2  # exact in float32 for this format
+    got = oracle.encode_e4m3(mid.astype(np.float32))
+    want = np.where(codes[:-1] % 2 == 0, codes[:-1], codes[1:])
+    assert np.array_equal(got, want)
+    above = oracle.encode_e4m3((mid * (1 + 1e-4)).astype(np.float32))
+    assert np.array_equal(above, codes[1:])
+    below = oracle.encode_e4m3((mid * (1 - 1e-4)).astype(np.float32))
+    assert np.array_equal(below, codes[:-1])
+    assert list(oracle.encode_e4m3(np.array([448, 449, 1e30, -1e30], np.float32))) == [0x7E, 0x7E, 0x7E, 0xFE]
+    assert oracle.encode_e4m3(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def test_encode_e4m3_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.normal(size=4000) * s for s in (1e-3, 1.0, 60.0)]).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode_e4m3(x), want)
+
+
+def test_rope_closed_forms():
+    rng = np.random.default_rng(6)
+    x = rng.normal(size=(3, 128)).astype(np.float32)
+    P = 4
+    cos_tab = np.ones((P, 32), np.float32)
+    sin_tab = np.zeros((P, 32), np.float32)
+    cos_tab[1], sin_tab[1] = 0.0, 1.0        # a quarter turn: (x0, x1) -> (-x1, x0) exactly
+    ang = rng.uniform(-np.pi, np.pi, 32)
+    cos_tab[2], sin_tab[2] = np.cos(ang), np.sin(ang)
+    assert np.array_equal(oracle.rope_f32(x, 0, cos_tab, sin_tab, 64), x)
+    q = oracle.rope_f32(x, 1, cos_tab, sin_tab, 64)
+    assert np.array_equal(q[:, 0:64:2], -x[:, 1:64:2]) and np.array_equal(q[:, 1:64:2], x[:, 0:64:2])
+    assert np.array_equal(q[:, 64:], x[:, 64:])  # dims past the rope part are untouched
+    r = oracle.rope_f32(x, 2, cos_tab, sin_tab, 64).astype(np.float64)
+    c, s = cos_tab[2].astype(np.float64), sin_tab[2].astype(np.float64)
+    x0, x1 = x[:, 0:64:2].astype(np.float64), x[:, 1:64:2].astype(np.float64)
+    assert np.allclose(r[:, 0:64:2], x0 * c - x1 * s, rtol=0, atol=1e-6)
+    assert np.allclose(r[:, 1:64:2], x0 * s + x1 * c, rtol=0, atol=1e-6)
+
+
+def test_quantize_row_e4m3_properties():
+    rng = np.random.default_rng(8)
+    x = (rng.normal(size=(50, 128)) * rng.uniform(0.01, 100, size=(50, 1))).astype(np.float32)
+    x[3] = 0.0
+    codes, scale = oracle.quantize_row_e4m3(x)
+    assert scale[3] == 1.0 and not codes[3].any()
+    dec = oracle.decode_e4m3(codes) * scale[:, None].astype(np.float64)
+    amax = np.abs(x).max(axis=1)
+    for i in range(50):
+        if i == 3:
+            continue
+        j = np.argmax(np.abs(x[i]))
+        assert codes[i, j] in (0x7E, 0xFE)  # the largest entry takes the largest code
+        # round to nearest: half a step of 3 mantissa bits, or half the subnormal step
+        err = np.abs(dec[i] - x[i])
+        assert np.all(err <= np.maximum(np.abs(x[i]) / 16, 2.0 ** -10 * scale[i]) * (1 + 1e-6))
+    # the input recipe's quantiser (torch's cast) makes the same codes and scales
+    c2, s2 = dsa_inputs.quantize_e4m3_rows(torch.from_numpy(x))
+    assert np.array_equal(codes, c2.numpy()) and np.array_equal(scale, s2.numpy())
