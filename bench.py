@@ -10,6 +10,8 @@ Besides the end-to-end rate the line carries:
                 same row passes as dsa_forward makes), measured with HIP events on the stream
                 the kernels run on, and each stage's algorithmic rate;
   roofline      the dominant stage's achieved rate against its MI355X peak;
+  k_sweep       the whole forward on the same prefill for k = 512 .. 8192 (k = 2048 is the
+                headline configuration; the pages leave the choice of k open);
   decode        batched decode (32 sequences, lengths uniform in [32768, 131072]): the
                 forward step, the cache producer (RoPE + FP8 codes of the new tokens, cache
                 append) alone, and both together;
@@ -224,6 +226,34 @@ def decode_case(dev, steps):
                 cache_append_us=round(us_app, 2), us_per_step_with_append=round(us_all, 2))
 
 
+def k_sweep(c, ks, steps=2):
+    """The whole forward at the same length and inputs for several k (the inputs do not depend
+    on k): ms per step and tokens/s for each."""
+    import dataclasses
+
+    res = {}
+    for k in ks:
+        dims = dataclasses.replace(c["dims"], topk=k)
+        n = dsa.workspace_size(dims, c["batch"])
+        ws = c["ws"] if c["ws"].numel() >= n else torch.empty(n, dtype=torch.uint8, device=c["ws"].device)
+        i = c["inp"]
+
+        def fwd():
+            dsa.forward(dims, c["batch"], i["q8"], i["q_scale"], i["w"], i["k8"], i["k_scale"], i["q"],
+                        i["kv"], c["out"], c["lse"], None, ws)
+
+        fwd()
+        torch.cuda.synchronize()
+        with Timer() as tm:
+            for _ in range(steps):
+                fwd()
+        ms = tm.ms() / steps
+        res[str(k)] = dict(ms_per_step=round(ms, 3), tokens_per_s=round(c["L"] / (ms / 1e3), 1))
+        del ws
+        log(f"k={k}: {ms:.2f} ms/step")
+    return res
+
+
 def cpu_baseline(c, budget_s=20.0, max_rows=192):
     """The oracle on uniformly spaced query rows of the same prefill (indexer over every
     earlier key, top-k, MQA).  Rows are processed in growing batches until ~budget_s."""
@@ -267,6 +297,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--k-sweep", default="512,1024,2048,4096,8192",
+                    help="comma-separated k values timed on the same prefill ('' to skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first copy BYTES between two device buffers (a plain copy of known size "
                          "that calibrates the HBM byte counters of a profiled run)")
@@ -344,6 +376,8 @@ def main():
         roof["avg_launch_ms"] = round(avg * 1e3, 3)
         line["roofline"] = roof
         log(f"stages {json.dumps(stages)}")
+    if args.k_sweep:
+        line["k_sweep"] = k_sweep(c, [int(x) for x in args.k_sweep.split(",")])
     if not args.no_decode:
         del c["out"]
         torch.cuda.empty_cache()

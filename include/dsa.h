@@ -24,13 +24,13 @@
  *    (causal, the query's own position included).  Prefill is one sequence with
  *    len_q = len_k; decode is len_q = 1 per sequence.
  *  - Validation: every argument is checked on the host before anything is enqueued (null
- *    pointers, unsupported dims, topk outside [1, 2048], len_q > len_k, non-monotone or
+ *    pointers, unsupported dims, topk outside [1, 8192], len_q > len_k, non-monotone or
  *    non-zero-based offsets, pointers not 16-byte aligned, strides too small or not a
  *    multiple of 4, workspace too small).  On error nothing is enqueued and nothing is
  *    written.  A failed kernel launch returns DSA_ERR_HIP.
  *  - Supported dims: (n_idx_heads, idx_dim, n_heads, qk_dim, v_dim) is either the
  *    DeepSeek-V3.2-Exp shape (64, 128, 128, 576, 512) or the tiny test shape
- *    (4, 32, 8, 80, 64); topk may be any value in [1, 2048]; sm_scale any positive
+ *    (4, 32, 8, 80, 64); topk may be any value in [1, 8192]; sm_scale any positive
  *    finite number.  Anything else returns DSA_ERR_UNSUPPORTED.
  */
 #ifndef DSA_H_
@@ -56,7 +56,7 @@ typedef enum {
 typedef struct {
     int32_t n_idx_heads; /* H_I: indexer heads (64)                                  */
     int32_t idx_dim;     /* d_I: indexer head dim (128)                              */
-    int32_t topk;        /* k: selected positions per query (2048)                   */
+    int32_t topk;        /* k: selected positions per query (2048; at most 8192)      */
     int32_t n_heads;     /* H: attention heads sharing each latent row (128)         */
     int32_t qk_dim;      /* latent row width used for the logits (576 = 512 + 64)    */
     int32_t v_dim;       /* value width = leading part of the latent row (512)       */
@@ -83,8 +83,8 @@ typedef struct {
     int32_t pages_per_seq;          /* >= ceil(max len_k / 64) when paged               */
 } dsa_batch;
 
-/* Bytes of workspace that dsa_forward (and dsa_sparse_mqa, which needs less) uses by
- * default for this batch.  dsa_forward also accepts a smaller workspace down to
+/* Bytes of workspace that dsa_forward uses by default for this batch (also enough for
+ * dsa_sparse_mqa and dsa_dense_mqa on the whole batch).  dsa_forward also accepts a smaller workspace down to
  * dsa_workspace_min; it then processes fewer query rows per pass. */
 dsa_status dsa_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
 dsa_status dsa_workspace_min(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
@@ -124,7 +124,7 @@ dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* s
                     hipStream_t stream);
 
 /* Workspace that lets dsa_topk split rows over several workgroups for this batch (0 when
- * the batch has 128 rows or more, or rows longer than 131072 scores). */
+ * the batch has 128 rows or more, rows longer than 131072 scores, or topk above 2048). */
 dsa_status dsa_topk_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
 
 /* Sparse MQA over the latent cache (stage 3).
@@ -142,10 +142,23 @@ dsa_status dsa_sparse_mqa(const dsa_dims* dims, const dsa_batch* batch, const ui
                           const uint16_t* kv, const int32_t* idx, uint16_t* out, float* lse,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Dense causal MQA: the attention above over every position s in [0, p] of query row i's
+ * sequence, without an index row.  For a row with p + 1 <= topk this is exactly what DSA
+ * computes (top-k keeps every earlier position); the pages name it the short-sequence
+ * masked-MHA mode (DSA deep dive, section 4, efficiency).  dsa_forward uses it for passes
+ * whose rows all have p + 1 <= topk.  Same layouts as dsa_sparse_mqa (dims->topk unused
+ * beyond validation); ws as there: needed when T < 128 (the rows are then split over
+ * workgroups by their length), sized by dsa_workspace_size. */
+dsa_status dsa_dense_mqa(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
+                         const uint16_t* kv, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* The whole hot path: indexer -> top-k -> sparse MQA, on the caller's stream.
  * Inputs as above.  Scores live only in the workspace, one pass of query rows at a time;
  * the full L x L score matrix never exists.  Rows with p + 1 <= topk skip the indexer and
- * the selection (their index set is every earlier position; the result is the same).
+ * the selection (their index set is every earlier position; the result is the same), and a
+ * pass whose rows all have p + 1 <= topk runs the dense causal attention of dsa_dense_mqa
+ * (index rows are then written only when idx_out is given).
  *   idx_out [T, topk] int32 or NULL (then the selected positions stay in the workspace). */
 dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
                        const float* q_scale, const float* w, const uint8_t* k8,

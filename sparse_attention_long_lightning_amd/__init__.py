@@ -5,8 +5,8 @@ device pointers together with the current HIP stream; every step of the computat
 the library's HIP kernels.  There is no fallback: if the library is missing, importing the
 functions raises.
 
-Entry points mirror the C ABI: ``indexer_scores``, ``topk``, ``sparse_mqa``, ``forward``,
-``workspace_size`` / ``workspace_min``.  A batch is described by its query and key row offsets
+Entry points mirror the C ABI: ``indexer_scores``, ``topk``, ``sparse_mqa``, ``dense_mqa``,
+``forward``, ``cache_append``, ``workspace_size`` / ``workspace_min`` / ``topk_workspace_size``.  A batch is described by its query and key row offsets
 (``cu_q``, ``cu_k``: B + 1 integers); see ``include/dsa.h`` for the layouts.
 """
 from __future__ import annotations
@@ -18,8 +18,8 @@ import numpy as np
 import torch
 
 __all__ = ["DsaError", "Dims", "Batch", "lib", "library_path", "indexer_scores", "topk",
-           "sparse_mqa", "forward", "workspace_size", "workspace_min", "PROD_DIMS", "TINY_DIMS",
-           "STATUS"]
+           "topk_workspace_size", "sparse_mqa", "dense_mqa", "forward", "cache_append",
+           "workspace_size", "workspace_min", "PROD_DIMS", "TINY_DIMS", "PAGE_SIZE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdsa.so")
@@ -119,6 +119,7 @@ def lib():
             "dsa_topk": [P, P, P, I64, P, P, S, P],
             "dsa_topk_workspace_size": [P, P, P],
             "dsa_sparse_mqa": [P, P, P, P, P, P, P, P, S, P],
+            "dsa_dense_mqa": [P, P, P, P, P, P, P, S, P],
             "dsa_forward": [P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
             "dsa_cache_append": [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P],
         }.items():
@@ -200,6 +201,15 @@ def sparse_mqa(dims, batch: Batch, q, kv, idx, out, lse=None, ws=None, stream=No
     _check(lib().dsa_sparse_mqa(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q), _ptr(kv),
                                 _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                 _stream(stream)), "dsa_sparse_mqa")
+    return out
+
+
+def dense_mqa(dims, batch: Batch, q, kv, out, lse=None, ws=None, stream=None):
+    """Causal attention of every query row over all earlier positions of its sequence."""
+    d = _dims(dims)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dsa_dense_mqa(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q), _ptr(kv), _ptr(out),
+                               _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)), "dsa_dense_mqa")
     return out
 
 

@@ -157,8 +157,10 @@ dsa_status dsa_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size
     if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
     if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
     const ForwardPlan p = plan_forward(dims, shape, bt, default_chunk(bt));
-    // dsa_sparse_mqa on the whole batch splits fewer than 128 rows over several workgroups
-    const size_t mqa = align_up(mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, dims->topk)));
+    // dsa_sparse_mqa and dsa_dense_mqa on the whole batch split fewer than 128 rows over
+    // several workgroups (by k, or by the longest row)
+    const int slots = dims->topk > bt.max_lk ? dims->topk : bt.max_lk;
+    const size_t mqa = align_up(mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, slots)));
     *bytes = p.total > mqa ? p.total : mqa;
     return DSA_OK;
 }
@@ -255,6 +257,26 @@ dsa_status dsa_sparse_mqa(const dsa_dims* dims, const dsa_batch* batch, const ui
     return hip_status(launch_sparse_mqa(a, map, bt.T, n_split, ws, stream));
 }
 
+dsa_status dsa_dense_mqa(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
+                         const uint16_t* kv, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!q || !kv || !out) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (lse != nullptr && !aligned16(lse)))
+        return DSA_ERR_INVALID_ARG;
+    const int n_split = mqa_splits(bt.T, bt.max_lk);
+    const size_t need = mqa_split_bytes(shape, bt.T, n_split);
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return DSA_ERR_WORKSPACE;
+    MqaArgs a{shape, q, kv, nullptr, dims->topk, out, lse, dims->sm_scale, IdxMode::Dense};
+    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
+    return hip_status(launch_sparse_mqa(a, map, bt.T, n_split, ws, stream));
+}
+
 dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
                        const float* q_scale, const float* w, const uint8_t* k8,
                        const float* k_scale, const uint16_t* q, const uint16_t* kv,
@@ -284,7 +306,8 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
         IndexerArgs ia{shape, q8, q_scale, w, k8, k_scale, sc, p.stride};
         RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
         const int n_split = mqa_splits(bt.T, topk);
-        MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale};
+        // the top-k rows hold their valid slots first: short rows read only p + 1 of them
+        MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale, IdxMode::Front};
         if (debug_log())
             fprintf(stderr, "[dsa] decode B=%d max_len_k=%d stride=%lld splits=%d\n", bt.B, bt.max_lk,
                     (long long)p.stride, n_split);
@@ -332,10 +355,13 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
                                            sc + (int64_t)(rsel - r0) * p.stride, stream);
             int32_t* ix = idx_out ? idx_out + (int64_t)(qb + r0) * topk : ix_ws;
             RowMap map{nullptr, nullptr, 1, qb + r0, pos0 + r0, kb};
-            if (e == hipSuccess)
+            // every row of the pass keeps all earlier positions (p + 1 <= k): dense causal
+            // attention, and the index rows only if the caller asked for them
+            const bool dense = pos0 + r1 <= topk;
+            if (e == hipSuccess && (!dense || idx_out != nullptr))
                 e = launch_topk(sc, p.stride, ix, topk, map, r1 - r0, pos0 + r1, wsb + p.tail_off, p.topk_bytes,
                                 stream);
-            MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale};
+            MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale, dense ? IdxMode::Dense : IdxMode::Front};
             if (e == hipSuccess) e = launch_sparse_mqa(ma, map, r1 - r0, 1, nullptr, stream);
             if (e != hipSuccess) return DSA_ERR_HIP;
         }

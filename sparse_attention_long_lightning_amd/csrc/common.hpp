@@ -15,7 +15,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kMaxTopk = 2048;
+constexpr int kMaxTopk = 8192;  // largest k accepted (k = 2048 in the DeepSeek-V3.2-Exp shape)
 
 // Maps a query row to its sequence, absolute position and key-row base.
 //  single-sequence mode (cu_q == nullptr): row i -> position pos0 + i, key base kbase,

@@ -41,15 +41,24 @@ hipError_t launch_topk(const float* scores, int64_t stride, int32_t* idx, int to
                        const RowMap& map, int n_rows, int max_len, void* ws, size_t ws_bytes,
                        hipStream_t st);
 
+// How the attention finds a row's key positions.
+enum class IdxMode : int {
+    General = 0,  // idx row of topk slots, -1 anywhere
+    Front = 1,    // idx row whose valid slots come first (top-k output): only the first
+                  // min(topk, p + 1) slots are read
+    Dense = 2,    // no idx: slot j holds position j for j <= p (dense causal attention)
+};
+
 struct MqaArgs {
     Shape shape;
     const uint16_t* q;
     const uint16_t* kv;
-    const int32_t* idx;  // row i of the launch at idx + i * topk
+    const int32_t* idx;  // row i of the launch at idx + i * topk (unused when Dense)
     int topk;
     uint16_t* out;       // indexed by packed query row
     float* lse;          // nullable, indexed by packed query row
     float sm_scale;
+    IdxMode mode = IdxMode::General;
 };
 
 // Bytes of split partials for n_rows rows split n_split ways.

@@ -5,22 +5,27 @@
 // rope; every head shares the row):
 //     z_s = sm * <q[t,h,:], c_s>,  out[t,h,:] = sum_s softmax(z)_s c_s[:512],  lse = ln sum e^z
 //
+// Slots: a row's key positions come from its index row (any slot may be -1), from the first
+// min(k, p + 1) slots of an index row whose valid slots come first (the top-k output), or,
+// for dense causal attention (the short-sequence masked-MHA mode of the DeepSeek-V3.2-Exp
+// deep dive, section 4), from the positions 0 .. p themselves.
+//
 // Work decomposition: one workgroup = one query row x 64 heads (two workgroups per row of 128
 // heads, issued 8 ids apart so both run on the same XCD and the second gather of each latent
-// row hits its L2).  Its 4 waves are 2 head groups (32 heads) x 2 halves; a half owns half of
-// the 576 logit dims (query fragments stay in registers) and half of the 512 value dims
-// (fp32 accumulators).  Per block of 32 selected rows:
-//   gather   direct global->LDS loads (no staging registers) in a three-deep ring, so the
-//            loads of the next two blocks fly while this one computes;
-//   S^T      = C Q^T with v_mfma_f32_32x32x16_bf16 (A = latent rows from LDS, M = rows;
-//            B = query heads, N = heads) over the wave's dims; the halves' partial tiles are
-//            summed through LDS (both waves form S0 + S1 in the same order);
-//   softmax  online, in base 2; lane l owns head l%32, so running max and sum are per lane
-//            (one exchange with lane l^32); O is rescaled only when a block max exceeds the
-//            running max by more than 16 (2^16 of headroom in fp32 and bf16 P);
-//   O^T      += V^T P^T with A = value columns read by ds_read_b64_tr_b16 straight from the
-//            row-major block and B = P^T taken from the S^T accumulators (the S^T row order
-//            puts 8 consecutive block rows in each lane per 16-row k-slice).
+// row hits its L2); with few rows, each row's slots are also split over workgroups whose
+// (m, l, O) partials a combine kernel merges.  Per block of 32 slots the 8 waves (wave w
+// shares its SIMD with wave w + 4) work in three roles:
+//   waves 0, 1  logits S^T = C Q^T (v_mfma_f32_32x32x16_bf16; A = latent rows from LDS,
+//               B = the query heads of one 32-head group, kept in registers) over the first
+//               half of the 576 dims; then the sum with the other half, masking, the base-2
+//               online softmax (lane l owns head l % 32; O is rescaled only when a block max
+//               exceeds the running max by more than 16) and P^T published to LDS;
+//   waves 4, 5  the other half of the same group's logits, handed over through LDS and
+//               computed one block ahead, so their MFMAs run beside the softmax of waves 0, 1
+//               on the same SIMD; they also issue the direct global->LDS loads of the block
+//               three steps ahead into a four-block ring;
+//   waves 2, 3, 6, 7  O^T += V^T P^T for all 64 heads over a quarter of the 512 value dims,
+//               A = value columns read by ds_read_b64_tr_b16 straight from the row-major block.
 // LDS rows are XOR-swizzled in 16-byte chunks so that the 16 rows read together by an A
 // operand, and the 4 consecutive rows of a transpose read, fall in distinct bank groups.
 #include <type_traits>
@@ -222,7 +227,7 @@ template <int H, int DQK, int DV, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     int topk, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, RowMap map, int n_rows, int n_split, float sm_log2) {
+    float2* __restrict__ part_ml, RowMap map, int n_rows, int n_split, float sm_log2, int mode) {
     using C = MqaCfg<H, DQK, DV>;
     using RV = typename C::RV;
     using RR = typename C::RR;
@@ -252,11 +257,15 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
     const RowInfo ri = row_info(map, row);
-    const int per = SPLIT ? (((topk + n_split - 1) / n_split + kBlk - 1) / kBlk) * kBlk : topk;
+    // slots of the row: all topk index slots, the first min(topk, p + 1) of a row whose
+    // valid slots come first, or the p + 1 positions of dense causal attention
+    const bool dense = mode == (int)IdxMode::Dense;
+    const int jn = dense ? ri.pos + 1 : mode == (int)IdxMode::Front ? min(topk, ri.pos + 1) : topk;
+    const int per = SPLIT ? (((jn + n_split - 1) / n_split + kBlk - 1) / kBlk) * kBlk : jn;
     const int j0 = split * per;
-    const int j1 = min(topk, j0 + per);
+    const int j1 = min(jn, j0 + per);
     const int nblk = j1 > j0 ? (j1 - j0 + kBlk - 1) / kBlk : 0;
-    const int32_t* irow = idx + (int64_t)row * topk;
+    const int32_t* irow = dense ? nullptr : idx + (int64_t)row * topk;
     // latent rows are addressed from the sequence's first row (packed caches) or from the
     // start of the page pool (paged caches)
     const bool paged = map.pages != nullptr;
@@ -277,7 +286,8 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     };
     auto load_ids = [&](int b) {
         const int j = j0 + b * kBlk + lane;
-        return (lane < kBlk && j < j1) ? irow[j] : -1;
+        if (lane >= kBlk || j >= j1) return -1;
+        return dense ? j : irow[j];
     };
     if (wv < C::RING && wv < nblk) stage(wv, load_ids(wv));
     __syncthreads();
@@ -694,14 +704,14 @@ hipError_t launch_t(const MqaArgs& a, const RowMap& map, int n_rows, int n_split
     if (n_split <= 1) {
         hipLaunchKernelGGL((sparse_mqa_kernel<H, DQK, DV, false>), dim3(grid_x<C>(n_rows)), dim3(C::THREADS), 0,
                            st, a.q, a.kv, a.idx, a.topk, a.out, a.lse, nullptr, nullptr, map, n_rows,
-                           1, sm_log2);
+                           1, sm_log2, (int)a.mode);
         return hipGetLastError();
     }
     float* part_o = (float*)ws;
     float2* part_ml = (float2*)(part_o + (size_t)n_rows * n_split * H * DV);
     hipLaunchKernelGGL((sparse_mqa_kernel<H, DQK, DV, true>), dim3(grid_x<C>(n_rows), n_split), dim3(C::THREADS),
                        0, st, a.q, a.kv, a.idx, a.topk, a.out, a.lse, part_o, part_ml, map, n_rows,
-                       n_split, sm_log2);
+                       n_split, sm_log2, (int)a.mode);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((mqa_combine_kernel<H, DV>), dim3(n_rows, (H + 3) / 4), dim3(256), 0, st,

@@ -378,6 +378,8 @@ constexpr int kMaxSegs = 8;   // segments per row the merge holds in LDS
 // Fewer rows than this are split (one workgroup per row would leave most CUs idle); with
 // more, one workgroup per row is faster, as it keeps no candidates in memory.
 constexpr int kSplitRows = 128;
+// Largest k of the segmented path (the merge holds kMaxSegs * k candidates in LDS).
+constexpr int kSegMaxTopk = 2048;
 
 struct SelSmem {
     uint32_t hist[kBins1];
@@ -595,8 +597,8 @@ __global__ __launch_bounds__(kThreads, 2) void topk_segment_kernel(
 __global__ __launch_bounds__(kThreads, 1) void topk_merge_kernel(
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos, int32_t* __restrict__ idx,
     int topk, RowMap map, int n_rows, int n_segs) {
-    __shared__ __attribute__((aligned(16))) uint32_t keys[kMaxSegs * kMaxTopk];
-    __shared__ __attribute__((aligned(16))) int32_t pos[kMaxSegs * kMaxTopk];
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kMaxSegs * kSegMaxTopk];
+    __shared__ __attribute__((aligned(16))) int32_t pos[kMaxSegs * kSegMaxTopk];
     __shared__ SelSmem sm;
     const int row = blockIdx.x;
     if (row >= n_rows) return;
@@ -646,7 +648,7 @@ int topk_segments(int max_len) { return (max_len + kSeg - 1) / kSeg; }
 
 size_t topk_ws_bytes(int n_rows, int max_len, int topk) {
     const int ns = topk_segments(max_len);
-    if (ns > kMaxSegs || n_rows <= 0 || n_rows >= kSplitRows) return 0;
+    if (ns > kMaxSegs || n_rows <= 0 || n_rows >= kSplitRows || topk > kSegMaxTopk) return 0;
     return (size_t)n_rows * ns * topk * (sizeof(uint32_t) + sizeof(int32_t));
 }
 

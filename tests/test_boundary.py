@@ -58,7 +58,7 @@ def dims_with(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(topk=0), INVALID), (dict(topk=2049), INVALID), (dict(topk=-5), INVALID),
+    (dict(topk=0), INVALID), (dict(topk=8193), INVALID), (dict(topk=-5), INVALID),
     (dict(sm_scale=0.0), INVALID), (dict(sm_scale=float("nan")), INVALID),
     (dict(sm_scale=float("inf")), INVALID), (dict(n_idx_heads=32), UNSUPPORTED),
     (dict(idx_dim=64), UNSUPPORTED), (dict(n_heads=64), UNSUPPORTED), (dict(qk_dim=512), UNSUPPORTED),

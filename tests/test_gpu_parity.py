@@ -153,8 +153,8 @@ def topk_ws(dims, batch, split, cuda):
     return torch.empty(n, dtype=torch.uint8, device=cuda)
 
 
-@pytest.mark.parametrize("split", [False, True])
-@pytest.mark.parametrize("k", [2048, 32, 1])
+@pytest.mark.parametrize("k,split", [(2048, False), (2048, True), (32, False), (32, True), (1, False),
+                                     (1, True), (4096, False), (8192, False)])
 def test_topk_bit_exact_on_identical_arrays(cuda, k, split):
     say(f"topk adversarial rows k={k} split={split}")
     rng = np.random.default_rng(7 + k)
