@@ -298,3 +298,39 @@ def cache_append(q_idx, k_idx, pos, cos_tab, sin_tab, rope_dim: int):
         b, sb = quantize_row_e4m3(rope_f32(k_idx[i], p, cos_tab, sin_tab, rope_dim))
         q8.append(a); qs.append(sa); k8.append(b); ks.append(sb)
     return np.stack(q8), np.stack(qs), np.stack(k8), np.array(ks, np.float32)
+
+
+def indexer_kl(q_bits, kv_bits, lse, slots, scores, sm_scale: float):
+    """Indexer training target and its KL divergences, forward only (DeepSeek-V3.2-Exp
+    overview, "训练"; 解析 §二; deep dive §3): for query row t over its slot positions S_t
+    (every s <= p in the dense warm-up, the selected set in the sparse stage),
+        P_t[s] = sum_h exp(z[t,h,s] - lse[t,h]),   z = sm_scale * q[t,h,:] . kv[s,:]
+    (the main attention probabilities summed over heads), L1-normalised over S_t, and
+        Q_t = softmax over S_t of the indexer scores I[t,s];
+    returns (KL(P_t || Q_t), KL(Q_t || P_t)) per row, 0 for a row without slots.
+      q_bits [T, H, Dqk] uint16 (bf16), kv_bits [S, Dqk] uint16 (the rows of the row's
+      sequence), lse [T, H] float (natural log), slots: T arrays of positions (-1 = empty),
+      scores: T arrays with I[t, s] at index s."""
+    q = decode_bf16(q_bits)
+    kv = decode_bf16(kv_bits)
+    lse = np.asarray(lse, np.float64)
+    T = q.shape[0]
+    kl = np.zeros(T)
+    rev = np.zeros(T)
+    for t in range(T):
+        pos = np.asarray(slots[t], np.int64)
+        pos = pos[pos >= 0]
+        if len(pos) == 0:
+            continue
+        z = sm_scale * (kv[pos] @ q[t].T)                  # [slots, H]
+        P = np.exp(z - lse[t][None, :]).sum(axis=1)
+        P = P / P.sum()
+        I = np.asarray(scores[t], np.float64)[pos]
+        m = I.max()
+        logQ = I - (m + np.log(np.exp(I - m).sum()))
+        Q = np.exp(logQ)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            logP = np.log(P)
+            kl[t] = np.sum(np.where(P > 0, P * (logP - logQ), 0.0))
+            rev[t] = np.sum(Q * (logQ - logP))
+    return kl, rev

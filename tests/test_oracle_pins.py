@@ -425,3 +425,77 @@ def test_quantize_row_e4m3_properties():
     # the input recipe's quantiser (torch's cast) makes the same codes and scales
     c2, s2 = dsa_inputs.quantize_e4m3_rows(torch.from_numpy(x))
     assert np.array_equal(codes, c2.numpy()) and np.array_equal(scale, s2.numpy())
+
+
+# ---- indexer KL target ----------------------------------------------------------------
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_indexer_kl_uniform_target_closed_form():
+    # a zero query gives every slot the same logit, so P is uniform over the n slots and
+    # KL(U || Q) = -ln n - mean(log Q), KL(Q || U) = sum Q log Q + ln n
+    rng = np.random.default_rng(21)
+    H, D, n = 3, 8, 7
+    q = _bf16_bits(np.zeros((1, H, D)))
+    kv = _bf16_bits(rng.normal(size=(n, D)))
+    lse = np.full((1, H), np.log(n))
+    I = rng.normal(size=n) * 2.0
+    kl, rev = oracle.indexer_kl(q, kv, lse, [np.arange(n)], [I], 0.5)
+    logQ = I - np.log(np.exp(I).sum())
+    assert np.isclose(kl[0], -np.log(n) - logQ.mean(), rtol=0, atol=1e-12)
+    assert np.isclose(rev[0], np.sum(np.exp(logQ) * logQ) + np.log(n), rtol=0, atol=1e-12)
+
+
+def test_indexer_kl_two_slots_worked_example():
+    # one head, two slots with logits 0 and ln 3 (q = [1, 0], rows [0, *] and [ln 3, *],
+    # sm_scale 1): P = (1/4, 3/4); indexer scores (0, 0): Q = (1/2, 1/2)
+    # KL(P || Q) = 1/4 ln(1/2) + 3/4 ln(3/2) ; KL(Q || P) = 1/2 ln 2 + 1/2 ln(2/3)
+    ln3 = float(np.log(np.float32(3.0)))
+    q = _bf16_bits([[[1.0, 0.0]]])
+    kvf = np.array([[0.0, 5.0], [ln3, -2.0]], np.float32)
+    kv = _bf16_bits(kvf)
+    z1 = float(oracle.decode_bf16(kv)[1, 0])  # the bf16 value of ln 3
+    lse = np.array([[np.log(1.0 + np.exp(z1))]])
+    kl, rev = oracle.indexer_kl(q, kv, lse, [np.array([0, 1])], [np.zeros(2)], 1.0)
+    p1 = np.exp(z1) / (1 + np.exp(z1))
+    p0 = 1 - p1
+    assert np.isclose(kl[0], p0 * np.log(2 * p0) + p1 * np.log(2 * p1), rtol=0, atol=1e-12)
+    assert np.isclose(rev[0], 0.5 * np.log(0.5 / p0) + 0.5 * np.log(0.5 / p1), rtol=0, atol=1e-12)
+    assert abs(p1 - 0.75) < 2e-3  # bf16 rounding of ln 3 only
+
+
+def test_indexer_kl_matches_scipy_and_properties():
+    from scipy.special import rel_entr, softmax
+    rng = np.random.default_rng(22)
+    H, D, S = 4, 16, 40
+    qf = rng.normal(size=(3, H, D))
+    kvf = rng.normal(size=(S, D))
+    q, kv = _bf16_bits(qf), _bf16_bits(kvf)
+    qd, kvd = oracle.decode_bf16(q), oracle.decode_bf16(kv)
+    slots = [np.arange(S), np.r_[rng.permutation(S)[:10], -1, -1], np.array([-1, 5, -1])]
+    scores = [rng.normal(size=S) * 3 for _ in range(3)]
+    # lse of each head over the row's own slots (as the attention reports it)
+    lse = np.zeros((3, H))
+    for t in range(3):
+        p = slots[t][slots[t] >= 0]
+        z = 0.3 * kvd[p] @ qd[t].T
+        lse[t] = np.log(np.exp(z).sum(axis=0))
+    kl, rev = oracle.indexer_kl(q, kv, lse, slots, scores, 0.3)
+    for t in range(3):
+        p = slots[t][slots[t] >= 0]
+        P = softmax(0.3 * kvd[p] @ qd[t].T, axis=0).mean(axis=1)  # per-head softmax, head mean
+        Q = softmax(scores[t][p])
+        assert np.isclose(kl[t], rel_entr(P, Q).sum(), rtol=1e-12, atol=1e-12)
+        assert np.isclose(rev[t], rel_entr(Q, P).sum(), rtol=1e-12, atol=1e-12)
+        assert kl[t] >= 0 and rev[t] >= 0
+    assert kl[2] == 0 and rev[2] == 0  # one slot: P = Q = 1
+    # Q equal to P: both divergences vanish
+    p = slots[0]
+    P = softmax(0.3 * kvd[p] @ qd[0].T, axis=0).mean(axis=1)
+    kl0, rev0 = oracle.indexer_kl(q[:1], kv, lse[:1], [p], [np.log(P) + 7.0], 0.3)
+    assert abs(kl0[0]) < 1e-12 and abs(rev0[0]) < 1e-12
+    # a row without slots
+    kl1, rev1 = oracle.indexer_kl(q[:1], kv, lse[:1], [np.array([-1, -1])], [scores[0]], 0.3)
+    assert kl1[0] == 0 and rev1[0] == 0
