@@ -41,6 +41,7 @@ METRIC = "DSA prefill tokens/s at 128K (+ indexer FP8 TFLOP/s); decode µs/token
 PEAK = {"fp8": 5000.0, "bf16": 2500.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s (MI355X)
 FLOP_INDEXER_PAIR = 2 * 64 * 128       # per causal (query, key) pair
 FLOP_MQA_PAIR = 2 * 128 * (576 + 512)  # per selected (query, key) pair
+FLOP_KL_PAIR = 2 * 128 * 576           # per slot of the indexer KL target (logits only)
 
 
 # HBM traffic per launch of a kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
@@ -136,6 +137,8 @@ def stage_breakdown(c, reps=1):
     stride = (L + 3) // 4 * 4
     scores = c["ws"][: ch * stride * 4].view(torch.float32).view(ch, stride)
     idx = torch.empty(ch, k, dtype=torch.int32, device=dev)
+    kl = torch.empty(L, dtype=torch.float32, device=dev)
+    t_kl, n_kl = 0.0, 0
     t = {"indexer": 0.0, "topk": 0.0, "mqa": 0.0}
     launches = {"indexer": 0, "topk": 0, "mqa": 0}
     pairs_idx = 0
@@ -163,6 +166,12 @@ def stage_breakdown(c, reps=1):
                                c["ws"])
             t["mqa"] += tm.ms()
             launches["mqa"] += 1
+            # indexer KL target of the pass (training only; not part of the forward step)
+            with Timer() as tm:
+                dsa.indexer_kl(dims, b, inp["q"][r0:r1], inp["kv"], c["lse"][r0:r1], idx, scores, stride,
+                               kl[r0:r1])
+            t_kl += tm.ms()
+            n_kl += 1
             pairs_mqa += sum(min(p + 1, k) for p in range(r0, r1))
     for s in t:
         t[s] /= reps
@@ -171,7 +180,7 @@ def stage_breakdown(c, reps=1):
     topk_rows = sum(1 for p in range(L) if p + 1 > k)
     topk_bytes = 4 * pairs_idx + 8 * 1024 * L  # one read of every valid score + the index rows
     return t, launches, dict(indexer_pairs=pairs_idx, mqa_pairs=pairs_mqa, topk_rows=topk_rows,
-                             topk_bytes=topk_bytes)
+                             topk_bytes=topk_bytes, kl_ms=t_kl / reps, kl_launches=n_kl // reps)
 
 
 def sum_range(lo, hi):
@@ -354,6 +363,10 @@ def main():
                              frac_bf16_peak=round(tf_mqa / PEAK["bf16"], 4),
                              tokens_per_s=round(L / (t["mqa"] / 1e3), 1))
         line["stages"] = stages
+        tf_kl = work["mqa_pairs"] * FLOP_KL_PAIR / (work["kl_ms"] / 1e3) / 1e12
+        line["kl_target"] = dict(ms=round(work["kl_ms"], 3), launches=work["kl_launches"],
+                                 tflops=round(tf_kl, 1), frac_bf16_peak=round(tf_kl / PEAK["bf16"], 4),
+                                 note="indexer KL target over the top-k slots, forward only")
         line["indexer_fp8_tflops"] = round(tf_idx, 1)
         dom = max(t, key=lambda s: t[s])
         if dom == "indexer":

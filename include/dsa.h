@@ -166,6 +166,26 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
                        uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* Indexer training target, forward only (DeepSeek-V3.2-Exp overview, "训练": the dense
+ * warm-up aligns the indexer with the main attention summed over heads and L1-normalised,
+ * and the sparse stage does the same on the selected set only; 解析 §二).  For query row i
+ * over its slots S_i (the non-(-1) entries of idx[i,:], or every position s in [0, p] when
+ * idx is NULL):
+ *   P_i[s] = sum_h exp(sm_scale * q[i,h,:] . kv[s,:] - lse[i,h]),  then P_i /= sum_s P_i[s]
+ *   Q_i    = softmax over S_i of the indexer scores I[i,s]
+ *   kl[i]  = KL(P_i || Q_i) = sum_s P log(P / Q);  kl_rev[i] = KL(Q_i || P_i)  (+inf if some
+ *            slot has P = 0);  0 for a row without slots.
+ * The pages write the divergence with its arguments in both orders; both are returned.
+ *   q, kv   as for dsa_sparse_mqa (packed or paged caches);  idx [T, topk] int32 or NULL
+ *   lse     [T, n_heads] float32: natural-log LSE of the attention over the same slots (what
+ *           dsa_sparse_mqa with this idx, or dsa_dense_mqa, return)
+ *   scores  float32 row i at scores + i*score_stride, entry s = I[i,s] for every slot s
+ *           (what dsa_indexer_scores writes); score_stride >= max len_k, multiple of 4
+ *   kl [T] float32;  kl_rev [T] float32 or NULL. */
+dsa_status dsa_indexer_kl(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
+                          const uint16_t* kv, const float* lse, const int32_t* idx, const float* scores,
+                          int64_t score_stride, float* kl, float* kl_rev, hipStream_t stream);
+
 /* Decode cache producer (the indexer's RoPE + FP8 step before the selection: DeepSeek-V3.2-Exp
  * lightning-indexer walk-through, step 2 — rotary encoding of the first 64 dims of the indexer
  * query and key, FP8 quantisation of both, the key codes and their scale kept in the cache).

@@ -6,7 +6,7 @@ the library's HIP kernels.  There is no fallback: if the library is missing, imp
 functions raises.
 
 Entry points mirror the C ABI: ``indexer_scores``, ``topk``, ``sparse_mqa``, ``dense_mqa``,
-``forward``, ``cache_append``, ``workspace_size`` / ``workspace_min`` / ``topk_workspace_size``.  A batch is described by its query and key row offsets
+``forward``, ``cache_append``, ``indexer_kl``, ``workspace_size`` / ``workspace_min`` / ``topk_workspace_size``.  A batch is described by its query and key row offsets
 (``cu_q``, ``cu_k``: B + 1 integers); see ``include/dsa.h`` for the layouts.
 """
 from __future__ import annotations
@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = ["DsaError", "Dims", "Batch", "lib", "library_path", "indexer_scores", "topk",
-           "topk_workspace_size", "sparse_mqa", "dense_mqa", "forward", "cache_append",
+           "topk_workspace_size", "sparse_mqa", "dense_mqa", "forward", "cache_append", "indexer_kl",
            "workspace_size", "workspace_min", "PROD_DIMS", "TINY_DIMS", "PAGE_SIZE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -121,6 +121,7 @@ def lib():
             "dsa_sparse_mqa": [P, P, P, P, P, P, P, P, S, P],
             "dsa_dense_mqa": [P, P, P, P, P, P, P, S, P],
             "dsa_forward": [P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
+            "dsa_indexer_kl": [P, P, P, P, P, P, P, I64, P, P, P],
             "dsa_cache_append": [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P],
         }.items():
             fn = getattr(L, name)
@@ -226,6 +227,18 @@ def forward(dims, batch: Batch, q8, q_scale, w, k8, k_scale, q, kv, out, lse=Non
 
 PROD_DIMS = Dims(64, 128, 2048, 128, 576, 512, 1.0 / np.sqrt(192.0))
 TINY_DIMS = Dims(4, 32, 32, 8, 80, 64, 1.0 / np.sqrt(80.0))
+
+
+def indexer_kl(dims, batch: Batch, q, kv, lse, idx, scores, score_stride: int, kl, kl_rev=None,
+               stream=None):
+    """KL(P || softmax(I)) (and the reverse when kl_rev is given) per query row, P the
+    heads-summed attention over the row's slots (idx rows, or every earlier position when
+    idx is None)."""
+    d = _dims(dims)
+    _check(lib().dsa_indexer_kl(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q), _ptr(kv), _ptr(lse),
+                                _ptr(idx), _ptr(scores), int(score_stride), _ptr(kl), _ptr(kl_rev),
+                                _stream(stream)), "dsa_indexer_kl")
+    return kl
 
 
 def cache_append(dims, batch: Batch, q_idx, k_idx, kv_new, rope_cos, rope_sin, q8, q_scale,

@@ -369,6 +369,26 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
     return DSA_OK;
 }
 
+dsa_status dsa_indexer_kl(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
+                          const uint16_t* kv, const float* lse, const int32_t* idx, const float* scores,
+                          int64_t score_stride, float* kl, float* kl_rev, hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!q || !kv || !lse || !scores || !kl) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(lse) || !aligned16(scores) || !aligned16(kl) ||
+        (idx != nullptr && !aligned16(idx)) || (kl_rev != nullptr && !aligned16(kl_rev)))
+        return DSA_ERR_INVALID_ARG;
+    if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
+    KlArgs a{shape, q, kv, lse, idx, dims->topk, idx ? IdxMode::General : IdxMode::Dense, scores, score_stride,
+             kl, kl_rev, dims->sm_scale};
+    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
+    return hip_status(launch_indexer_kl(a, map, bt.T, stream));
+}
+
 dsa_status dsa_cache_append(const dsa_dims* dims, const dsa_batch* batch, const float* q_idx,
                             const float* k_idx, const uint16_t* kv_new, const float* rope_cos,
                             const float* rope_sin, int32_t n_pos, uint8_t* q8, float* q_scale,

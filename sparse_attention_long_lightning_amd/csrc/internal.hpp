@@ -86,4 +86,23 @@ struct CacheAppendArgs {
 // written at each token's cache row.
 hipError_t launch_cache_append(const CacheAppendArgs& a, const RowMap& map, int n_rows, hipStream_t st);
 
+struct KlArgs {
+    Shape shape;
+    const uint16_t* q;      // [T, H, qk_dim] bf16
+    const uint16_t* kv;     // latent cache rows (packed or paged, see RowMap)
+    const float* lse;       // [T, H] natural-log LSE of the attention over the same slots
+    const int32_t* idx;     // [T, topk] slot positions (unused when Dense)
+    int topk;
+    IdxMode mode;
+    const float* scores;    // indexer scores, row i at scores + i * stride, index = position
+    int64_t stride;
+    float* kl;              // [T] KL(P || softmax(I))
+    float* kl_rev;          // [T] KL(softmax(I) || P) or nullptr
+    float sm_scale;
+};
+
+// KL divergences between the heads-summed attention distribution and the indexer's softmax
+// over each row's slots (one workgroup per row).
+hipError_t launch_indexer_kl(const KlArgs& a, const RowMap& map, int n_rows, hipStream_t st);
+
 }  // namespace dsa

@@ -191,3 +191,24 @@ def test_workspace_size_covers_the_attention_split_of_small_batches():
     need = dsa.workspace_size(d, b)
     assert dsa.lib().dsa_sparse_mqa(ctypes.byref(d), ctypes.byref(b.c), FAKE, FAKE, FAKE, FAKE, None,
                                     FAKE, need - 16, None) == WORKSPACE
+
+
+def test_indexer_kl_rejects_bad_arguments():
+    d, b = dims_with(), cpu_batch([0, 4], [0, 100])
+    lib = dsa.lib()
+
+    def call(q=FAKE, kv=FAKE, lse=FAKE, idx=FAKE, scores=FAKE, stride=100, kl=FAKE, rev=None):
+        return lib.dsa_indexer_kl(ctypes.byref(d), ctypes.byref(b.c), q, kv, lse, idx, scores, stride, kl,
+                                  rev, None)
+    for name in ("q", "kv", "lse", "scores", "kl"):
+        assert call(**{name: None}) == INVALID, name
+        assert call(**{name: FAKE + 4}) == INVALID, name
+    assert call(idx=FAKE + 4) == INVALID
+    assert call(rev=FAKE + 8) == INVALID
+    assert call(stride=96) == INVALID    # shorter than the longest row
+    assert call(stride=102) == INVALID   # not a multiple of 4
+    assert lib.dsa_indexer_kl(ctypes.byref(dims_with(n_heads=64)), ctypes.byref(b.c), FAKE, FAKE, FAKE, None,
+                              FAKE, 100, FAKE, None, None) == UNSUPPORTED
+    e = cpu_batch([0, 0], [0, 7])
+    assert lib.dsa_indexer_kl(ctypes.byref(d), ctypes.byref(e.c), None, None, None, None, None, 8, None, None,
+                              None) == OK  # no rows
