@@ -52,7 +52,7 @@ KERNEL_SOURCES = {
                           "sparse_attention_long_lightning_amd/csrc/common.hpp"],
     "indexer_prefill_kernel": ["sparse_attention_long_lightning_amd/csrc/indexer.hip",
                                "sparse_attention_long_lightning_amd/csrc/common.hpp"],
-    "topk_kernel": ["sparse_attention_long_lightning_amd/csrc/topk.hip",
+    "topk_hist_kernel": ["sparse_attention_long_lightning_amd/csrc/topk.hip",
                     "sparse_attention_long_lightning_amd/csrc/common.hpp"],
 }
 
@@ -127,8 +127,10 @@ def chunk_rows(c):
 
 
 def stage_breakdown(c, reps=1):
-    """Runs the three stage entry points on the same row passes dsa_forward makes and times
-    every launch with HIP events.  Returns per-stage totals (ms) and algorithmic work."""
+    """Runs the stage entry points on the same row passes dsa_forward makes (the indexer that
+    also counts each row's scores, the top-k that starts from those counts, the sparse MQA)
+    and times every call with HIP events.  Returns per-stage totals (ms) and algorithmic
+    work."""
     dims, inp, L = c["dims"], c["inp"], c["L"]
     k = dims.topk
     dev = inp["q8"].device
@@ -137,6 +139,7 @@ def stage_breakdown(c, reps=1):
     stride = (L + 3) // 4 * 4
     scores = c["ws"][: ch * stride * 4].view(torch.float32).view(ch, stride)
     idx = torch.empty(ch, k, dtype=torch.int32, device=dev)
+    counts = torch.empty(ch, dsa.COUNT_BINS, dtype=torch.int32, device=dev)
     kl = torch.empty(L, dtype=torch.float32, device=dev)
     t_kl, n_kl = 0.0, 0
     t = {"indexer": 0.0, "topk": 0.0, "mqa": 0.0}
@@ -152,13 +155,14 @@ def stage_breakdown(c, reps=1):
             if rsel < r1:
                 bs = dsa.Batch([0, r1 - rsel], [0, r1], device=dev)
                 with Timer() as tm:
-                    dsa.indexer_scores(dims, bs, inp["q8"][rsel:], inp["q_scale"][rsel:], inp["w"][rsel:],
-                                       inp["k8"], inp["k_scale"], scores[rsel - r0:], stride)
+                    dsa.indexer_scores_counted(dims, bs, inp["q8"][rsel:], inp["q_scale"][rsel:], inp["w"][rsel:],
+                                               inp["k8"], inp["k_scale"], scores[rsel - r0:], stride,
+                                               counts[rsel - r0:])
                 t["indexer"] += tm.ms()
                 launches["indexer"] += 1
                 pairs_idx += sum_range(rsel + 1, r1)
             with Timer() as tm:
-                dsa.topk(dims, b, scores, stride, idx)
+                dsa.topk_counted(dims, b, scores, stride, counts, idx)
             t["topk"] += tm.ms()
             launches["topk"] += 1
             with Timer() as tm:
@@ -382,7 +386,7 @@ def main():
         else:
             per = work["topk_bytes"] / launches["topk"] / 1e9
             avg = t["topk"] / launches["topk"] / 1e3
-            roof = dict(kernel="topk_kernel", bound="hbm", achieved=round(per / avg, 1),
+            roof = dict(kernel="topk_hist_kernel", bound="hbm", achieved=round(per / avg, 1),
                         peak=PEAK["hbm"], unit="GB/s")
         roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
         roof["traffic"] = recorded_traffic(roof["kernel"])

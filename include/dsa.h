@@ -127,6 +127,24 @@ dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* s
  * the batch has 128 rows or more, rows longer than 131072 scores, or topk above 2048). */
 dsa_status dsa_topk_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
 
+/* Fused indexer -> top-k, as two calls (what dsa_forward does in each prefill pass).
+ * dsa_indexer_scores_counted: dsa_indexer_scores for a prefill batch (a sequence with several
+ *   query rows; decode batches and paged caches: DSA_ERR_UNSUPPORTED) that also counts, per
+ *   query row, the scores it stores that are >= +0 by their order-preserving 32-bit key
+ *   (bits 30..21, i.e. sign, exponent and two mantissa bits of the score):
+ *   counts [T, DSA_COUNT_BINS] uint32, cleared by the call.
+ * dsa_topk_counted: dsa_topk from those scores and counts.  The counts give the selection's
+ *   first radix digit without reading the row, so each row is read once (rows with fewer
+ *   than topk scores >= +0, or too many candidates for on-chip memory, fall back to the
+ *   two-read selection).  The result is identical to dsa_topk. */
+#define DSA_COUNT_BINS 1024
+dsa_status dsa_indexer_scores_counted(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                                      const float* q_scale, const float* w, const uint8_t* k8,
+                                      const float* k_scale, float* scores, int64_t score_stride,
+                                      uint32_t* counts, hipStream_t stream);
+dsa_status dsa_topk_counted(const dsa_dims* dims, const dsa_batch* batch, const float* scores,
+                            int64_t score_stride, const uint32_t* counts, int32_t* idx, hipStream_t stream);
+
 /* Sparse MQA over the latent cache (stage 3).
  * For query row i and head h, over the slots of idx[i,:] that are not -1 (positions in
  * the row's own sequence; trusted to lie in [0, len_k)):

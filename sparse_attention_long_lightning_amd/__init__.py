@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = ["DsaError", "Dims", "Batch", "lib", "library_path", "indexer_scores", "topk",
-           "topk_workspace_size", "sparse_mqa", "dense_mqa", "forward", "cache_append", "indexer_kl",
+           "topk_workspace_size", "indexer_scores_counted", "topk_counted", "COUNT_BINS", "sparse_mqa", "dense_mqa", "forward", "cache_append", "indexer_kl",
            "workspace_size", "workspace_min", "PROD_DIMS", "TINY_DIMS", "PAGE_SIZE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -118,6 +118,8 @@ def lib():
             "dsa_indexer_scores": [P, P, P, P, P, P, P, P, I64, P],
             "dsa_topk": [P, P, P, I64, P, P, S, P],
             "dsa_topk_workspace_size": [P, P, P],
+            "dsa_indexer_scores_counted": [P, P, P, P, P, P, P, P, I64, P, P],
+            "dsa_topk_counted": [P, P, P, I64, P, P, P],
             "dsa_sparse_mqa": [P, P, P, P, P, P, P, P, S, P],
             "dsa_dense_mqa": [P, P, P, P, P, P, P, S, P],
             "dsa_forward": [P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
@@ -176,6 +178,27 @@ def indexer_scores(dims, batch: Batch, q8, q_scale, w, k8, k_scale, scores, scor
                                     _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(scores),
                                     int(score_stride), _stream(stream)), "dsa_indexer_scores")
     return scores
+
+
+COUNT_BINS = 1024  # per-row score counts of the fused indexer -> top-k (DSA_COUNT_BINS)
+
+
+def indexer_scores_counted(dims, batch: Batch, q8, q_scale, w, k8, k_scale, scores, score_stride: int,
+                           counts, stream=None):
+    """indexer_scores for a prefill batch, also filling counts [T, COUNT_BINS] (uint32 / int32)."""
+    d = _dims(dims)
+    _check(lib().dsa_indexer_scores_counted(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q8), _ptr(q_scale),
+                                            _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(scores), int(score_stride),
+                                            _ptr(counts), _stream(stream)), "dsa_indexer_scores_counted")
+    return scores, counts
+
+
+def topk_counted(dims, batch: Batch, scores, score_stride: int, counts, idx, stream=None):
+    """topk starting from the counts of indexer_scores_counted (one read of each row)."""
+    d = _dims(dims)
+    _check(lib().dsa_topk_counted(ctypes.byref(d), ctypes.byref(batch.c), _ptr(scores), int(score_stride),
+                                  _ptr(counts), _ptr(idx), _stream(stream)), "dsa_topk_counted")
+    return idx
 
 
 def topk_workspace_size(dims, batch: Batch) -> int:

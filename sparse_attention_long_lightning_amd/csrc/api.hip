@@ -107,19 +107,23 @@ dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_
 struct ForwardPlan {
     int64_t stride = 0;
     int chunk = 0;  // prefill rows per pass
-    size_t scores_off = 0, idx_off = 0, tail_off = 0, topk_bytes = 0, total = 0;
+    size_t scores_off = 0, idx_off = 0, hist_off = 0, tail_off = 0, topk_bytes = 0, total = 0;
 };
 
-// Workspace layout of dsa_forward: [scores | idx (when idx_out is NULL) | tail], where the
-// tail holds the top-k candidates and, later on the same stream, the MQA split partials.
+// Workspace layout of dsa_forward: [scores | idx (when idx_out is NULL) | hist | tail].
+// Prefill: hist holds the indexer's per-row score counts that the top-k starts from.
+// Decode: the tail holds the top-k candidates and, later on the same stream, the MQA split
+// partials.
 ForwardPlan plan_forward(const dsa_dims* d, Shape shape, const Batch& bt, int chunk) {
     ForwardPlan p;
     p.stride = score_stride_for(bt);
     p.chunk = bt.decode ? bt.T : chunk;
     p.scores_off = 0;
     p.idx_off = align_up((size_t)p.chunk * p.stride * sizeof(float));
-    p.tail_off = p.idx_off + align_up((size_t)p.chunk * d->topk * sizeof(int32_t));
-    p.topk_bytes = topk_ws_bytes(p.chunk, bt.max_lk, d->topk);
+    p.hist_off = p.idx_off + align_up((size_t)p.chunk * d->topk * sizeof(int32_t));
+    const size_t hist_bytes = bt.decode ? 0 : (size_t)p.chunk * kHistBins * sizeof(uint32_t);
+    p.tail_off = p.hist_off + align_up(hist_bytes);
+    p.topk_bytes = bt.decode ? topk_ws_bytes(p.chunk, bt.max_lk, d->topk) : 0;
     size_t tail = p.topk_bytes;
     if (bt.decode) {
         const size_t mqa = mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, d->topk));
@@ -178,10 +182,11 @@ dsa_status dsa_workspace_min(const dsa_dims* dims, const dsa_batch* batch, size_
     return DSA_OK;
 }
 
-dsa_status dsa_indexer_scores(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
-                              const float* q_scale, const float* w, const uint8_t* k8,
-                              const float* k_scale, float* scores, int64_t score_stride,
-                              hipStream_t stream) {
+namespace {
+
+dsa_status indexer_scores(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
+                          const float* w, const uint8_t* k8, const float* k_scale, float* scores,
+                          int64_t score_stride, uint32_t* counts, hipStream_t stream) {
     Shape shape;
     Batch bt;
     dsa_status st;
@@ -193,20 +198,58 @@ dsa_status dsa_indexer_scores(const dsa_dims* dims, const dsa_batch* batch, cons
         !aligned16(k_scale) || !aligned16(scores))
         return DSA_ERR_INVALID_ARG;
     if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
+    if (counts != nullptr && (!aligned16(counts))) return DSA_ERR_INVALID_ARG;
     IndexerArgs a{shape, q8, q_scale, w, k8, k_scale, scores, score_stride};
-    if (bt.decode)
+    if (bt.decode) {
+        if (counts != nullptr) return DSA_ERR_UNSUPPORTED;  // counts come from the prefill kernel
         return hip_status(launch_indexer_decode(a, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, bt.pages,
                                                 bt.pages_per_seq, stream));
+    }
     if (bt.pages != nullptr) return DSA_ERR_UNSUPPORTED;  // paged caches: decode batches only
+    if (counts != nullptr && launch_zero_words(counts, (int64_t)bt.T * kHistBins, stream) != hipSuccess)
+        return DSA_ERR_HIP;
     for (int b = 0; b < bt.B; ++b) {
         const int lq = bt.lq(b), lk = bt.lk(b);
         if (lq == 0) continue;
         const int row0 = batch->cu_q_host[b];
         hipError_t e = launch_indexer_prefill(a, row0, lq, lk - lq, batch->cu_k_host[b],
-                                              scores + (int64_t)row0 * score_stride, stream);
+                                              scores + (int64_t)row0 * score_stride, stream,
+                                              counts ? counts + (int64_t)row0 * kHistBins : nullptr);
         if (e != hipSuccess) return DSA_ERR_HIP;
     }
     return DSA_OK;
+}
+
+}  // namespace
+
+dsa_status dsa_indexer_scores(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                              const float* q_scale, const float* w, const uint8_t* k8,
+                              const float* k_scale, float* scores, int64_t score_stride,
+                              hipStream_t stream) {
+    return indexer_scores(dims, batch, q8, q_scale, w, k8, k_scale, scores, score_stride, nullptr, stream);
+}
+
+dsa_status dsa_indexer_scores_counted(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                                      const float* q_scale, const float* w, const uint8_t* k8,
+                                      const float* k_scale, float* scores, int64_t score_stride,
+                                      uint32_t* counts, hipStream_t stream) {
+    if (counts == nullptr) return DSA_ERR_INVALID_ARG;
+    return indexer_scores(dims, batch, q8, q_scale, w, k8, k_scale, scores, score_stride, counts, stream);
+}
+
+dsa_status dsa_topk_counted(const dsa_dims* dims, const dsa_batch* batch, const float* scores,
+                            int64_t score_stride, const uint32_t* counts, int32_t* idx, hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!scores || !idx || !counts || !aligned16(scores) || !aligned16(idx) || !aligned16(counts))
+        return DSA_ERR_INVALID_ARG;
+    if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
+    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
+    return hip_status(launch_topk_from_hist(scores, score_stride, counts, idx, dims->topk, map, bt.T, stream));
 }
 
 dsa_status dsa_topk_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes) {
@@ -324,9 +367,8 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
     const int64_t stride = score_stride_for(bt);
     // the idx area is reserved even when idx_out is given (plan_forward's layout)
     auto bytes_for = [&](int c) { return plan_forward(dims, shape, bt, c).total; };
-    // first estimate from the per-row areas (top-k candidates are only kept for passes of
-    // fewer than 128 rows); bytes_for then gives the exact size
-    const size_t per_row = (size_t)stride * sizeof(float) + (size_t)topk * 4;
+    // first estimate from the per-row areas; bytes_for then gives the exact size
+    const size_t per_row = (size_t)stride * sizeof(float) + (size_t)topk * 4 + kHistBins * 4;
     int64_t c64 = (int64_t)(ws_bytes / per_row);
     int chunk = (int)(c64 < bt.max_lq ? c64 : bt.max_lq);
     if (chunk > kRowGranule) chunk -= chunk % kRowGranule;
@@ -336,6 +378,7 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
     const ForwardPlan p = plan_forward(dims, shape, bt, chunk);
     float* sc = (float*)(wsb + p.scores_off);
     int32_t* ix_ws = (int32_t*)(wsb + p.idx_off);
+    uint32_t* hs = (uint32_t*)(wsb + p.hist_off);
     IndexerArgs ia{shape, q8, q_scale, w, k8, k_scale, sc, p.stride};
     if (debug_log())
         fprintf(stderr, "[dsa] prefill B=%d T=%d chunk=%d stride=%lld\n", bt.B, bt.T, chunk,
@@ -350,17 +393,19 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
             int rsel = topk - pos0;
             if (rsel < r0) rsel = r0;
             hipError_t e = hipSuccess;
-            if (rsel < r1)
+            // the indexer counts each row's scores for the top-k as it stores them
+            uint32_t* hrows = hs + (int64_t)(rsel - r0) * kHistBins;
+            if (rsel < r1) e = launch_zero_words(hrows, (int64_t)(r1 - rsel) * kHistBins, stream);
+            if (e == hipSuccess && rsel < r1)
                 e = launch_indexer_prefill(ia, qb + rsel, r1 - rsel, pos0 + rsel, kb,
-                                           sc + (int64_t)(rsel - r0) * p.stride, stream);
+                                           sc + (int64_t)(rsel - r0) * p.stride, stream, hrows);
             int32_t* ix = idx_out ? idx_out + (int64_t)(qb + r0) * topk : ix_ws;
             RowMap map{nullptr, nullptr, 1, qb + r0, pos0 + r0, kb};
             // every row of the pass keeps all earlier positions (p + 1 <= k): dense causal
             // attention, and the index rows only if the caller asked for them
             const bool dense = pos0 + r1 <= topk;
             if (e == hipSuccess && (!dense || idx_out != nullptr))
-                e = launch_topk(sc, p.stride, ix, topk, map, r1 - r0, pos0 + r1, wsb + p.tail_off, p.topk_bytes,
-                                stream);
+                e = launch_topk_from_hist(sc, p.stride, hs, ix, topk, map, r1 - r0, stream);
             MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale, dense ? IdxMode::Dense : IdxMode::Front};
             if (e == hipSuccess) e = launch_sparse_mqa(ma, map, r1 - r0, 1, nullptr, stream);
             if (e != hipSuccess) return DSA_ERR_HIP;

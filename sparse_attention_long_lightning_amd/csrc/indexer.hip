@@ -76,12 +76,15 @@ template <int H, int D>
 __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, float* __restrict__ scores,
-    int64_t stride, int row0, int n_rows, int pos0, int kbase) {
+    int64_t stride, int row0, int n_rows, int pos0, int kbase, uint32_t* __restrict__ hist) {
     using T = IxTile<D>;
     constexpr int NMT = (H + 15) / 16;  // 16-head M tiles per token
     constexpr int KGRP = D / 32;        // 32-byte K groups that carry data (D = 32 or 128)
     static_assert(D % 32 == 0 && D <= 128, "indexer head dim must be 32..128 in steps of 32");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kIxBufs * T::BYTES];
+    // per token of the workgroup, counts of the stored non-negative scores by key bits 30..21
+    // (top-k's first digit, upper half), two 16-bit bins per word; at most kIxSeg per bin
+    __shared__ uint32_t hcount[kIxTokens][kHistBins / 2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -97,6 +100,10 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
     if (seg0 > pmax) return;  // segment entirely above the causal diagonal
     const int seg_end = min(seg0 + kIxSeg, pmax + 1);
     const int ntiles = (seg_end - seg0 + kIxTile - 1) / kIxTile;
+    if (hist != nullptr) {  // each wave clears the counts of its own two tokens
+        uint32_t* hc = &hcount[2 * wv][0];
+        for (int j = lane; j < kHistBins; j += kWave) hc[j] = 0u;
+    }
 
     // Query fragments and folded head weights of this wave's two tokens.  Every load is
     // issued unconditionally from a clamped (valid) address and masked afterwards, so they
@@ -196,7 +203,16 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         for (int slot = 0; slot < 8; ++slot) {
             const int g = 2 * slot + g_odd;
             const int s = held_key0 + 16 * g + col;
-            if (g < held_groups && s <= my_pos) scores[my_row * stride + s] = held[slot];
+            if (g < held_groups && s <= my_pos) {
+                scores[my_row * stride + s] = held[slot];
+                if (hist != nullptr) {
+                    const uint32_t key = score_key(held[slot]);
+                    if (key >> 31) {
+                        const uint32_t b = (key >> 21) & (kHistBins - 1);
+                        atomicAdd(&hcount[2 * wv + tok][b >> 1], 1u << ((b & 1) << 4));
+                    }
+                }
+            }
         }
         held_groups = 0;
     };
@@ -315,6 +331,19 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         held_groups = ngroups;
     }
     flush();
+    if (hist != nullptr) {  // add this segment's counts to the rows' histograms
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {
+            if (tpos[tok] < 0) continue;
+            uint32_t* hrow = hist + (int64_t)trow[tok] * kHistBins;
+            const uint32_t* hc = &hcount[2 * wv + tok][0];
+            for (int j = lane; j < kHistBins / 2; j += kWave) {
+                const uint32_t v = hc[j];
+                if (v & 0xffffu) atomicAdd(&hrow[2 * j], v & 0xffffu);
+                if (v >> 16) atomicAdd(&hrow[2 * j + 1], v >> 16);
+            }
+        }
+    }
 }
 
 constexpr int kDecodeThreads = 256;
@@ -433,13 +462,13 @@ __global__ __launch_bounds__(kDecodeThreads) void indexer_decode_kernel(
 
 template <int H, int D>
 hipError_t launch_prefill_t(const IndexerArgs& a, int row0, int n_rows, int pos0, int kbase,
-                            float* scores, hipStream_t st) {
+                            float* scores, uint32_t* hist, hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
     const int pmax = pos0 + n_rows - 1;
     dim3 grid((n_rows + kIxTokens - 1) / kIxTokens, pmax / kIxSeg + 1);
     hipLaunchKernelGGL((indexer_prefill_kernel<H, D>), grid, dim3(kIxThreads), 0, st, a.q8,
                        a.q_scale, a.w, a.k8, a.k_scale, scores, a.score_stride, row0, n_rows,
-                       pos0, kbase);
+                       pos0, kbase, hist);
     return hipGetLastError();
 }
 
@@ -456,9 +485,9 @@ hipError_t launch_decode_t(const IndexerArgs& a, int n_seqs, int max_keys, const
 }  // namespace
 
 hipError_t launch_indexer_prefill(const IndexerArgs& a, int row0, int n_rows, int pos0,
-                                  int kbase, float* scores, hipStream_t st) {
-    if (a.shape == Shape::Prod) return launch_prefill_t<64, 128>(a, row0, n_rows, pos0, kbase, scores, st);
-    return launch_prefill_t<4, 32>(a, row0, n_rows, pos0, kbase, scores, st);
+                                  int kbase, float* scores, hipStream_t st, uint32_t* hist) {
+    if (a.shape == Shape::Prod) return launch_prefill_t<64, 128>(a, row0, n_rows, pos0, kbase, scores, hist, st);
+    return launch_prefill_t<4, 32>(a, row0, n_rows, pos0, kbase, scores, hist, st);
 }
 
 hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,

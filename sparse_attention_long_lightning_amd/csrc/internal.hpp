@@ -24,8 +24,11 @@ struct IndexerArgs {
 // Prefill tiles for rows [row0, row0 + n_rows) of one sequence whose first row sits at
 // position pos0 and whose key rows start at kbase.  Row i of the launch writes
 // scores + i * score_stride.
+// With hist != nullptr, row i also adds its stored non-negative scores to the kHistBins
+// counts at hist + i * kHistBins (key bits 30..21 of score_key; the counts must start at 0).
+constexpr int kHistBins = 1024;
 hipError_t launch_indexer_prefill(const IndexerArgs& a, int row0, int n_rows, int pos0,
-                                  int kbase, float* scores, hipStream_t st);
+                                  int kbase, float* scores, hipStream_t st, uint32_t* hist = nullptr);
 // Decode: one query row per sequence (cu_q[b+1] - cu_q[b] == 1); row cu_q[b] of the scores.
 // Paged caches: pages != nullptr (see RowMap).
 hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,
@@ -37,6 +40,12 @@ hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,
 // row) rows are split over several workgroups; without one (or for rows too long for the
 // split) one workgroup selects each row.  Both give the same result.
 size_t topk_ws_bytes(int n_rows, int max_len, int topk);
+// Top-k of rows whose non-negative scores the indexer counted into hist (kHistBins per row):
+// one read of each row when it holds at least topk non-negative scores; the same result.
+hipError_t launch_topk_from_hist(const float* scores, int64_t stride, const uint32_t* hist, int32_t* idx,
+                                 int topk, const RowMap& map, int n_rows, hipStream_t st);
+// p[0 .. n) = 0 (a kernel, so that the call can be captured in a graph).
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t st);
 hipError_t launch_topk(const float* scores, int64_t stride, int32_t* idx, int topk,
                        const RowMap& map, int n_rows, int max_len, void* ws, size_t ws_bytes,
                        hipStream_t st);

@@ -122,21 +122,9 @@ __device__ __forceinline__ int wave_slot(int f, int& total) {
     return incl - f;
 }
 
-__global__ __launch_bounds__(kThreads, 2) void topk_kernel(const float* __restrict__ scores,
-                                                           int64_t stride, int32_t* __restrict__ idx,
-                                                           int topk, RowMap map, int n_rows) {
-    __shared__ Smem sm;
-    const int row = blockIdx.x;
-    if (row >= n_rows) return;
-    const RowInfo ri = row_info(map, row);
-    const int n = ri.pos + 1;
-    int32_t* out = idx + (int64_t)row * topk;
+// Selects the top-k of the row x[0..n) (n > topk) into out, in position order.
+__device__ void select_row(Smem& sm, const float* __restrict__ x, int n, int topk, int32_t* __restrict__ out) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (n <= topk) {  // every candidate is selected
-        for (int j = tid; j < topk; j += kThreads) out[j] = j < n ? j : -1;
-        return;
-    }
-    const float* x = scores + (int64_t)row * stride;
     const int seg = ((n + kWaves - 1) / kWaves + 255) & ~255;
     const int sb = min(n, wv * seg), se = min(n, sb + seg);
 
@@ -360,6 +348,22 @@ __global__ __launch_bounds__(kThreads, 2) void topk_kernel(const float* __restri
             }
         run += total;
     }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void topk_kernel(const float* __restrict__ scores,
+                                                           int64_t stride, int32_t* __restrict__ idx,
+                                                           int topk, RowMap map, int n_rows) {
+    __shared__ Smem sm;
+    const int row = blockIdx.x;
+    if (row >= n_rows) return;
+    const RowInfo ri = row_info(map, row);
+    const int n = ri.pos + 1;
+    int32_t* out = idx + (int64_t)row * topk;
+    if (n <= topk) {  // every candidate is selected
+        for (int j = threadIdx.x; j < topk; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    select_row(sm, scores + (int64_t)row * stride, n, topk, out);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -642,6 +646,180 @@ __global__ __launch_bounds__(kThreads, 1) void topk_merge_kernel(
     emit_ordered(keys, total, theta, topk - above, sm, [&](int j, uint32_t, int slot) { out[slot] = pos[j]; });
 }
 
+// ---------------------------------------------------------------------------------------
+// Selection from an indexer-built histogram (fused indexer -> top-k).
+//
+// The prefill indexer counts, per query row, the scores whose key has the top bit set (the
+// non-negative scores) in 1024 bins of key bits 30..21, which are exactly bins 1024..2047 of
+// the first digit above.  When the row has at least k such scores, the threshold digit b1
+// and the list size follow from these counts alone, so the row is read once: every element
+// of digit >= b1 goes to the LDS list (in any order), digits 2 and 3 are resolved on the
+// list, and the selection is put back in position order through two position bitmaps (keys
+// above the threshold; ties at it, of which the lowest-positioned are taken).  Rows with
+// fewer than k non-negative scores, lists beyond LDS or rows longer than the bitmaps take
+// select_row.  The result is the same unique selection.
+constexpr int kBitmapWords = kCap / 2;     // each bitmap takes half of the list's key array
+constexpr int kFusedMaxLen = kBitmapWords * 32;
+
+struct FusedSmem {
+    uint32_t key[kCap];  // list keys; later the two position bitmaps
+    int32_t pos[kCap];   // list positions; class bits 30..31 after the threshold is known
+    SelSmem sel;
+    int count;
+};
+
+union TopkSmem {
+    Smem full;
+    FusedSmem fused;
+};
+
+__global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                const uint32_t* __restrict__ hist,
+                                                                int32_t* __restrict__ idx, int topk, RowMap map,
+                                                                int n_rows) {
+    __shared__ __attribute__((aligned(16))) TopkSmem smu;  // 16-byte key reads
+    FusedSmem& sm = smu.fused;
+    const int row = blockIdx.x;
+    if (row >= n_rows) return;
+    const RowInfo ri = row_info(map, row);
+    const int n = ri.pos + 1;
+    int32_t* out = idx + (int64_t)row * topk;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (n <= topk) {
+        for (int j = tid; j < topk; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    const float* x = scores + (int64_t)row * stride;
+    // ---- threshold digit from the counts ----
+    const uint32_t* h = hist + (int64_t)row * kHistBins;
+    int cnt = 0;
+    for (int b = tid; b < kHistBins; b += kThreads) {
+        const uint32_t c = h[b];
+        sm.sel.hist[b] = c;
+        cnt += (int)c;
+    }
+    int total;
+    block_exclusive_scan(cnt, sm.sel.wsum, total);  // also orders the histogram writes
+    bool fused = total >= topk && n <= kFusedMaxLen;
+    int b1 = 0, above1 = 0, nlist = 0;
+    if (fused) {
+        find_threshold(sm.sel.hist, kHistBins, topk, sm.sel);
+        b1 = kHistBins + sm.sel.sel_bin;
+        above1 = sm.sel.sel_above;
+        nlist = above1 + (int)sm.sel.hist[sm.sel.sel_bin];
+        fused = nlist <= kCap;
+    }
+    __syncthreads();  // every thread has read the threshold before the union is reused
+    if (!fused) {
+        select_row(smu.full, x, n, topk, out);
+        return;
+    }
+    // ---- one pass: every element of digit >= b1 into the list ----
+    if (tid == 0) sm.count = 0;
+    __syncthreads();
+    const int seg = ((n + kWaves - 1) / kWaves + 255) & ~255;
+    const int sb = min(n, wv * seg), se = min(n, sb + seg);
+    for (int e0 = sb; e0 < se; e0 += 256 * kUnroll) {
+        uint32_t k[kUnroll][4];
+        bool ok[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) load4(x, e0 + 256 * u + 4 * lane, se, k[u], ok[u]);
+        int f = 0;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ok[u][c] = ok[u][c] && (int)(k[u][c] >> 21) >= b1;
+                f += ok[u][c];
+            }
+        int wtot;
+        const int excl = wave_slot(f, wtot);
+        if (wtot == 0) continue;
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&sm.count, wtot);
+        base = __shfl(base, 0);
+        int j = base + excl;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (ok[u][c]) {
+                    if (j < kCap) {
+                        sm.key[j] = k[u][c];
+                        sm.pos[j] = e0 + 256 * u + 4 * lane + c;
+                    }
+                    ++j;
+                }
+    }
+    __syncthreads();
+    // ---- digits 2 and 3 on the list: theta, and how many ties at theta are taken ----
+    uint32_t theta;
+    int above;
+    lds_kth_key(sm.key, nlist, topk, sm.sel, theta, above);
+    const int need_eq = topk - above;
+    // classes: 1 = above theta, 2 = tie at theta, 0 = not selected
+    for (int j = tid; j < nlist; j += kThreads) {
+        const uint32_t kk = sm.key[j];
+        const int cls = kk > theta ? 1 : kk == theta ? 2 : 0;
+        sm.pos[j] |= cls << 30;
+    }
+    __syncthreads();  // the keys are dead: their array becomes the two bitmaps
+    const int W = (n + 31) >> 5;
+    uint32_t* bm_gt = sm.key;
+    uint32_t* bm_eq = sm.key + kBitmapWords;
+    for (int w = tid; w < W; w += kThreads) {
+        bm_gt[w] = 0u;
+        bm_eq[w] = 0u;
+    }
+    __syncthreads();
+    for (int j = tid; j < nlist; j += kThreads) {
+        const int v = sm.pos[j];
+        const int cls = (int)((uint32_t)v >> 30), p = v & 0x3fffffff;
+        if (cls == 1) atomicOr(&bm_gt[p >> 5], 1u << (p & 31));
+        else if (cls == 2) atomicOr(&bm_eq[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    // ---- emission in position order: thread t owns bitmap words [t*per, (t+1)*per) ----
+    const int per = (W + kThreads - 1) / kThreads;
+    const int w0 = min(W, tid * per), w1 = min(W, w0 + per);
+    int n_gt = 0, n_eq = 0;
+    for (int w = w0; w < w1; ++w) {
+        n_gt += __popc(bm_gt[w]);
+        n_eq += __popc(bm_eq[w]);
+    }
+    int t_gt, t_eq;
+    int r_gt = block_exclusive_scan(n_gt, sm.sel.wsum, t_gt);
+    int r_eq = block_exclusive_scan(n_eq, sm.sel.wsum, t_eq);
+    for (int w = w0; w < w1; ++w) {
+        const uint32_t g = bm_gt[w];
+        uint32_t e = bm_eq[w];
+        // keep the ties of rank < need_eq: the first (need_eq - r_eq) set bits of e
+        const int keep = need_eq - r_eq;
+        const int ne = __popc(e);
+        if (keep <= 0) {
+            e = 0u;
+        } else if (keep < ne) {
+            uint32_t m = e, kept = 0u;
+            for (int i = 0; i < keep; ++i) {
+                const uint32_t low = m & (~m + 1u);
+                kept |= low;
+                m ^= low;
+            }
+            e = kept;
+        }
+        r_eq += ne;
+        uint32_t sel = g | e;
+        int o = r_gt + min(r_eq - ne, need_eq);  // selected elements before this word
+        r_gt += __popc(g);
+        while (sel != 0u) {
+            const int b = __builtin_ctz(sel);
+            sel &= sel - 1u;
+            if (o < topk) out[o] = (w << 5) + b;
+            ++o;
+        }
+    }
+}
+
 }  // namespace
 
 int topk_segments(int max_len) { return (max_len + kSeg - 1) / kSeg; }
@@ -650,6 +828,27 @@ size_t topk_ws_bytes(int n_rows, int max_len, int topk) {
     const int ns = topk_segments(max_len);
     if (ns > kMaxSegs || n_rows <= 0 || n_rows >= kSplitRows || topk > kSegMaxTopk) return 0;
     return (size_t)n_rows * ns * topk * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
+hipError_t launch_topk_from_hist(const float* scores, int64_t stride, const uint32_t* hist, int32_t* idx,
+                                 int topk, const RowMap& map, int n_rows, hipStream_t st) {
+    if (n_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(n_rows), dim3(kThreads), 0, st, scores, stride, hist, idx, topk, map,
+                       n_rows);
+    return hipGetLastError();
+}
+
+namespace {
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* scores, int64_t stride, int32_t* idx, int topk,

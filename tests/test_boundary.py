@@ -212,3 +212,16 @@ def test_indexer_kl_rejects_bad_arguments():
     e = cpu_batch([0, 0], [0, 7])
     assert lib.dsa_indexer_kl(ctypes.byref(d), ctypes.byref(e.c), None, None, None, None, None, 8, None, None,
                               None) == OK  # no rows
+
+
+def test_counted_stages_reject_bad_arguments():
+    d, b = dims_with(), cpu_batch([0, 64], [0, 64])
+    lib = dsa.lib()
+    args = [FAKE] * 6
+    assert lib.dsa_indexer_scores_counted(ctypes.byref(d), ctypes.byref(b.c), *args, 64, None, None) == INVALID
+    assert lib.dsa_indexer_scores_counted(ctypes.byref(d), ctypes.byref(b.c), *args, 64, FAKE + 4, None) == INVALID
+    dec = cpu_batch([0, 1, 2], [0, 100, 300])  # decode batches are scored by the decode kernel: no counts
+    assert lib.dsa_indexer_scores_counted(ctypes.byref(d), ctypes.byref(dec.c), *args, 200, FAKE, None) == UNSUPPORTED
+    assert lib.dsa_topk_counted(ctypes.byref(d), ctypes.byref(b.c), FAKE, 64, None, FAKE, None) == INVALID
+    assert lib.dsa_topk_counted(ctypes.byref(d), ctypes.byref(b.c), FAKE, 64, FAKE, None, None) == INVALID
+    assert lib.dsa_topk_counted(ctypes.byref(d), ctypes.byref(b.c), FAKE, 60, FAKE, FAKE, None) == INVALID
