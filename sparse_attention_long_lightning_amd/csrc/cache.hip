@@ -3,10 +3,12 @@
 // dims of the indexer query and key, then FP8 codes for both, the key codes and their scale
 // kept in the cache), plus the copy of the tokens' latent rows into the latent cache.
 //
-// One workgroup per new token; its 64 query heads and its key are 65 rows of idx_dim values.
-// A row is held by one wave, lane l holding the pair (2l, 2l+1), which is exactly the pair the
-// rotation mixes, so the rotation is in-lane and the row's amax one wave reduction.  Bound:
-// HBM (32 KiB of fp32 query per token in, 8 KiB of codes out).
+// Each new token has 65 rows of idx_dim values (its 64 query heads and its key) and one latent
+// row.  One wave per row: lane l holds the pair (2l, 2l+1), which is exactly the pair the
+// rotation mixes, so the rotation is in-lane and the row's amax one wave reduction; a 256-thread
+// workgroup takes four rows of one token, the last one of each token also copies the latent
+// row.  Bound: HBM (32 KiB of fp32 query per token in, 8 KiB of codes out), i.e. latency at
+// decode sizes, hence one row per wave.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -15,6 +17,7 @@ namespace dsa {
 namespace {
 
 constexpr int kAppendThreads = 256;
+constexpr int kAppendRowsPerWg = kAppendThreads / kWave;
 
 // One row of D values (D/2 <= 64 pairs, one per lane): rotate the first R/2 pairs by the
 // table angle of position pos, then one scale (amax / 448, 1 for an all-zero row) and e4m3fn
@@ -61,23 +64,22 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
     float* __restrict__ q_scale, uint8_t* __restrict__ k8_cache, float* __restrict__ k_scale_cache,
     uint16_t* __restrict__ kv_cache, RowMap map, int n_rows) {
     static_assert(D % 4 == 0 && D / 2 <= kWave, "one pair per lane");
-    const int row = blockIdx.x;
+    constexpr int NG = (H + 1 + kAppendRowsPerWg - 1) / kAppendRowsPerWg;  // workgroups per token
+    const int row = blockIdx.x / NG, part = blockIdx.x % NG;
     if (row >= n_rows) return;
     const RowInfo ri = row_info(map, row);
     const int64_t crow = cache_row(map, ri, ri.pos);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    constexpr int NW = kAppendThreads / kWave;
     const float* cs = rope_cos + (int64_t)ri.pos * (D / 4);
     const float* sn = rope_sin + (int64_t)ri.pos * (D / 4);
     // rows 0 .. H-1: query heads; row H: the key
-    for (int v = wv; v <= H; v += NW) {
-        if (v < H)
-            rope_quant_row<D>(q_idx + ((int64_t)row * H + v) * D, cs, sn, lane, q8 + ((int64_t)row * H + v) * D,
-                              q_scale + (int64_t)row * H + v);
-        else
-            rope_quant_row<D>(k_idx + (int64_t)row * D, cs, sn, lane, k8_cache + crow * D, k_scale_cache + crow);
-    }
-    if (kv_new != nullptr) {  // the latent row, 16 bytes per thread
+    const int v = part * kAppendRowsPerWg + wv;
+    if (v < H)
+        rope_quant_row<D>(q_idx + ((int64_t)row * H + v) * D, cs, sn, lane, q8 + ((int64_t)row * H + v) * D,
+                          q_scale + (int64_t)row * H + v);
+    else if (v == H)
+        rope_quant_row<D>(k_idx + (int64_t)row * D, cs, sn, lane, k8_cache + crow * D, k_scale_cache + crow);
+    if (kv_new != nullptr && part == NG - 1) {  // the latent row, 16 bytes per thread
         constexpr int NP = DQK * 2 / 16;
         const uint4* s = (const uint4*)(kv_new + (int64_t)row * DQK);
         uint4* d = (uint4*)(kv_cache + crow * DQK);
@@ -85,16 +87,19 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
     }
 }
 
+template <int H>
+constexpr int append_groups() { return (H + 1 + kAppendRowsPerWg - 1) / kAppendRowsPerWg; }
+
 }  // namespace
 
 hipError_t launch_cache_append(const CacheAppendArgs& a, const RowMap& map, int n_rows, hipStream_t st) {
     if (n_rows <= 0) return hipSuccess;
     if (a.shape == Shape::Prod)
-        hipLaunchKernelGGL((cache_append_kernel<64, 128, 576>), dim3(n_rows), dim3(kAppendThreads), 0, st, a.q_idx,
+        hipLaunchKernelGGL((cache_append_kernel<64, 128, 576>), dim3(n_rows * append_groups<64>()), dim3(kAppendThreads), 0, st, a.q_idx,
                            a.k_idx, a.kv_new, a.rope_cos, a.rope_sin, a.q8, a.q_scale, a.k8_cache, a.k_scale_cache,
                            a.kv_cache, map, n_rows);
     else
-        hipLaunchKernelGGL((cache_append_kernel<4, 32, 80>), dim3(n_rows), dim3(kAppendThreads), 0, st, a.q_idx,
+        hipLaunchKernelGGL((cache_append_kernel<4, 32, 80>), dim3(n_rows * append_groups<4>()), dim3(kAppendThreads), 0, st, a.q_idx,
                            a.k_idx, a.kv_new, a.rope_cos, a.rope_sin, a.q8, a.q_scale, a.k8_cache, a.k_scale_cache,
                            a.kv_cache, map, n_rows);
     return hipGetLastError();

@@ -673,85 +673,11 @@ union TopkSmem {
     FusedSmem fused;
 };
 
-__global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __restrict__ scores, int64_t stride,
-                                                                const uint32_t* __restrict__ hist,
-                                                                int32_t* __restrict__ idx, int topk, RowMap map,
-                                                                int n_rows) {
-    __shared__ __attribute__((aligned(16))) TopkSmem smu;  // 16-byte key reads
-    FusedSmem& sm = smu.fused;
-    const int row = blockIdx.x;
-    if (row >= n_rows) return;
-    const RowInfo ri = row_info(map, row);
-    const int n = ri.pos + 1;
-    int32_t* out = idx + (int64_t)row * topk;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (n <= topk) {
-        for (int j = tid; j < topk; j += kThreads) out[j] = j < n ? j : -1;
-        return;
-    }
-    const float* x = scores + (int64_t)row * stride;
-    // ---- threshold digit from the counts ----
-    const uint32_t* h = hist + (int64_t)row * kHistBins;
-    int cnt = 0;
-    for (int b = tid; b < kHistBins; b += kThreads) {
-        const uint32_t c = h[b];
-        sm.sel.hist[b] = c;
-        cnt += (int)c;
-    }
-    int total;
-    block_exclusive_scan(cnt, sm.sel.wsum, total);  // also orders the histogram writes
-    bool fused = total >= topk && n <= kFusedMaxLen;
-    int b1 = 0, above1 = 0, nlist = 0;
-    if (fused) {
-        find_threshold(sm.sel.hist, kHistBins, topk, sm.sel);
-        b1 = kHistBins + sm.sel.sel_bin;
-        above1 = sm.sel.sel_above;
-        nlist = above1 + (int)sm.sel.hist[sm.sel.sel_bin];
-        fused = nlist <= kCap;
-    }
-    __syncthreads();  // every thread has read the threshold before the union is reused
-    if (!fused) {
-        select_row(smu.full, x, n, topk, out);
-        return;
-    }
-    // ---- one pass: every element of digit >= b1 into the list ----
-    if (tid == 0) sm.count = 0;
-    __syncthreads();
-    const int seg = ((n + kWaves - 1) / kWaves + 255) & ~255;
-    const int sb = min(n, wv * seg), se = min(n, sb + seg);
-    for (int e0 = sb; e0 < se; e0 += 256 * kUnroll) {
-        uint32_t k[kUnroll][4];
-        bool ok[kUnroll][4];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) load4(x, e0 + 256 * u + 4 * lane, se, k[u], ok[u]);
-        int f = 0;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                ok[u][c] = ok[u][c] && (int)(k[u][c] >> 21) >= b1;
-                f += ok[u][c];
-            }
-        int wtot;
-        const int excl = wave_slot(f, wtot);
-        if (wtot == 0) continue;
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&sm.count, wtot);
-        base = __shfl(base, 0);
-        int j = base + excl;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (ok[u][c]) {
-                    if (j < kCap) {
-                        sm.key[j] = k[u][c];
-                        sm.pos[j] = e0 + 256 * u + 4 * lane + c;
-                    }
-                    ++j;
-                }
-    }
-    __syncthreads();
+// The selection from a list of every candidate that can be selected (sm.key / sm.pos hold
+// nlist >= topk entries in any order; n is the row length, at most kFusedMaxLen): digits 2 and
+// 3 on the list give theta and the ties taken, then two position bitmaps give position order.
+__device__ void finish_from_list(FusedSmem& sm, int nlist, int topk, int n, int32_t* __restrict__ out) {
+    const int tid = threadIdx.x;
     // ---- digits 2 and 3 on the list: theta, and how many ties at theta are taken ----
     uint32_t theta;
     int above;
@@ -818,6 +744,96 @@ __global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __r
             ++o;
         }
     }
+}
+
+// The first digit from a row's counts: the threshold digit b1 and the number of elements of
+// digit >= b1; false when the list path does not apply (fewer than topk counted scores, more
+// than kCap candidates, or a row longer than the bitmaps).  Ends with a barrier.
+__device__ bool threshold_from_counts(FusedSmem& sm, const uint32_t* __restrict__ h, int n, int topk, int& b1,
+                                      int& nlist) {
+    int cnt = 0;
+    for (int b = threadIdx.x; b < kHistBins; b += kThreads) {
+        const uint32_t c = h[b];
+        sm.sel.hist[b] = c;
+        cnt += (int)c;
+    }
+    int total;
+    block_exclusive_scan(cnt, sm.sel.wsum, total);  // also orders the histogram writes
+    bool fused = total >= topk && n <= kFusedMaxLen;
+    b1 = 0;
+    nlist = 0;
+    if (fused) {
+        find_threshold(sm.sel.hist, kHistBins, topk, sm.sel);
+        b1 = kHistBins + sm.sel.sel_bin;
+        nlist = sm.sel.sel_above + (int)sm.sel.hist[sm.sel.sel_bin];
+        fused = nlist <= kCap;
+    }
+    __syncthreads();  // every thread has read the threshold before the shared memory is reused
+    return fused;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                const uint32_t* __restrict__ hist,
+                                                                int32_t* __restrict__ idx, int topk, RowMap map,
+                                                                int n_rows) {
+    __shared__ __attribute__((aligned(16))) TopkSmem smu;  // 16-byte key reads
+    FusedSmem& sm = smu.fused;
+    const int row = blockIdx.x;
+    if (row >= n_rows) return;
+    const RowInfo ri = row_info(map, row);
+    const int n = ri.pos + 1;
+    int32_t* out = idx + (int64_t)row * topk;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (n <= topk) {
+        for (int j = tid; j < topk; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    const float* x = scores + (int64_t)row * stride;
+    int b1, nlist;
+    const bool fused = threshold_from_counts(sm, hist + (int64_t)row * kHistBins, n, topk, b1, nlist);
+    if (!fused) {
+        select_row(smu.full, x, n, topk, out);
+        return;
+    }
+    // ---- one pass: every element of digit >= b1 into the list ----
+    if (tid == 0) sm.count = 0;
+    __syncthreads();
+    const int seg = ((n + kWaves - 1) / kWaves + 255) & ~255;
+    const int sb = min(n, wv * seg), se = min(n, sb + seg);
+    for (int e0 = sb; e0 < se; e0 += 256 * kUnroll) {
+        uint32_t k[kUnroll][4];
+        bool ok[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) load4(x, e0 + 256 * u + 4 * lane, se, k[u], ok[u]);
+        int f = 0;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ok[u][c] = ok[u][c] && (int)(k[u][c] >> 21) >= b1;
+                f += ok[u][c];
+            }
+        int wtot;
+        const int excl = wave_slot(f, wtot);
+        if (wtot == 0) continue;
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&sm.count, wtot);
+        base = __shfl(base, 0);
+        int j = base + excl;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (ok[u][c]) {
+                    if (j < kCap) {
+                        sm.key[j] = k[u][c];
+                        sm.pos[j] = e0 + 256 * u + 4 * lane + c;
+                    }
+                    ++j;
+                }
+    }
+    __syncthreads();
+    finish_from_list(sm, nlist, topk, n, out);
 }
 
 }  // namespace

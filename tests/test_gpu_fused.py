@@ -129,3 +129,35 @@ def test_counted_stages_match_the_plain_ones(cuda):
             k = k[(k >> 31) == 1]
             ref = np.bincount(((k >> 21) & 1023).astype(np.int64), minlength=1024)
             assert np.array_equal(hc[t], ref), f"seq {b} row {r}"
+
+
+def decode_unfused_idx(dims, inp, dev):
+    batch = dsa.Batch(inp["cu_q"], inp["cu_k"], device=dev)
+    T, L = batch.n_q, batch.max_len_k
+    stride = (L + 3) // 4 * 4
+    scores = torch.empty(T, stride, dtype=torch.float32, device=dev)
+    dsa.indexer_scores(dims, batch, inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"], scores, stride)
+    idx = torch.empty(T, dims.topk, dtype=torch.int32, device=dev)
+    dsa.topk(dims, batch, scores, stride, idx)
+    torch.cuda.synchronize()
+    return idx
+
+
+def test_decode_forward_topk_equals_two_stage(cuda):
+    # decode batches select with segment workgroups and a merge (no counts): the index rows of
+    # dsa_forward must equal dsa_indexer_scores + dsa_topk on one workgroup per row
+    dims = dsa_inputs.PROD
+    lens = [100, 2048, 2049, 16384, 16385, 40000, 91529, 131072, 70000, 30000]
+    say(f"decode forward index rows vs indexer_scores + topk, lens {lens}")
+    inp = dsa_inputs.decode_inputs(dims=dims, seed=11, device=cuda, lens=lens)
+    # row 8: negative head weights (few non-negative scores); row 9: one key repeated (ties)
+    inp["w"][8] = -inp["w"][8].abs()
+    k0 = inp["cu_k"][9]
+    inp["k8"][k0:k0 + lens[9]] = inp["k8"][k0]
+    inp["k_scale"][k0:k0 + lens[9]] = inp["k_scale"][k0]
+    a = fused_idx(dims, inp, cuda)
+    b = decode_unfused_idx(dims, inp, cuda)
+    bad = torch.nonzero((a != b).any(dim=1)).flatten().tolist()
+    assert not bad, f"decode rows differ: {bad}"
+    a2 = fused_idx(dims, inp, cuda)
+    assert torch.equal(a, a2)
