@@ -28,12 +28,10 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b) {
 __device__ __forceinline__ void materialize(const v8i& x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void materialize(float x) { asm volatile("" ::"v"(x)); }
 
-// p + w * ReLU(x) as two FMAs, using ReLU(x) = (x + |x|) / 2 with the 1/2 folded into w:
-// max-based forms cost an extra instruction to quiet the MFMA output first.  The two terms
-// cancel to within fp32 rounding of |w x| for x < 0, far below the FP8 products' own error.
-__device__ __forceinline__ float fma_relu_half(float w_half, float x, float p) {
-    return fmaf(w_half, fabsf(x), fmaf(w_half, x, p));
-}
+// The epilogues take p + w * ReLU(x) as two FMAs, w/2 * x and w/2 * |x|, using
+// ReLU(x) = (x + |x|) / 2 with the 1/2 folded into w: max-based forms cost an extra
+// instruction to quiet the MFMA output first.  The two terms cancel to within fp32 rounding
+// of |w x| for x < 0, far below the FP8 products' own error.
 
 // Sum over the four 16-lane groups; every lane ends with the total of its column.
 __device__ __forceinline__ float sum_over_groups(float v) {
@@ -132,7 +130,7 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
             for (int r = 0; r < 4; ++r) {
                 const int hh = mt * 16 + grp * 4 + r;
                 const int64_t e = qrow * H + min(hh, H - 1);
-                const float v = 0.5f * w[e] * qs[e];  // halved for fma_relu_half
+                const float v = 0.5f * w[e] * qs[e];  // halved: ReLU(x) = (x + |x|) / 2
                 wt[tok][mt][r] = (ok && hh < H) ? v : 0.f;
             }
         }
@@ -216,19 +214,6 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         }
         held_groups = 0;
     };
-    // Weighted ReLU sum over this lane's 16 heads of each token (the head sum is finished by
-    // reduce_pair across the four lane groups).
-    auto head_partials = [&](const v4f (&acc)[2][NMT], float (&part)[2]) {
-#pragma unroll
-        for (int tok = 0; tok < 2; ++tok) {
-            float p = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p = fma_relu_half(wt[tok][mt][r], acc[tok][mt][r], p);
-            part[tok] = p;
-        }
-    };
     // Sums the partials of groups 2s (pe) and 2s+1 (po) over the four lane groups with two
     // lane-swap rounds, leaving lane group r with group 2s + (r & 1) of token r >> 1 (the
     // layout flush expects), then applies that key's scale.
@@ -243,13 +228,6 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
             buf + T::KEY_BYTES + 4 * (16 * (2 * slot + (grp & 1)) + col));
         held[slot] = z * kscale;
     };
-    auto mfmas = [&](v4f (&acc)[2][NMT], const v8i& b) {
-#pragma unroll
-        for (int tok = 0; tok < 2; ++tok)
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], b);
-    };
-
     issue_tile(0);
     if (ntiles > 1) issue_tile(1);
     for (int t = 0; t < ntiles; ++t) {

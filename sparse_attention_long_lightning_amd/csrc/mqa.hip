@@ -111,7 +111,6 @@ __device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); 
 
 // Keeps a query fragment (an MFMA B operand, read as is from AGPRs) out of the VGPRs.
 __device__ __forceinline__ void pin_agpr(v8bf& x) { asm volatile("" : "+a"(x)); }
-__device__ __forceinline__ void pin_vgpr(v8bf& x) { asm volatile("" : "+v"(x)); }
 
 // f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
 template <int N, int I = 0, class F>
