@@ -253,14 +253,17 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         const int ngroups = min(kIxTile / 16, (tmax - key0) / 16 + 1);
 
         // The eight MFMAs of a group (token-major: k = 4*tok + mt) each run with the epilogue
-        // FMAs of the MFMA issued just before them, so the matrix pipe stays busy while the VALU
-        // works on a result that is already there; the last MFMA of a group is taken up under
-        // the first of the next.  Operand reads fly two groups ahead.  Every group of the tile
+        // FMAs of the MFMA issued DEP = 2 before them (1 with two MFMAs per group), so the
+        // matrix pipe stays busy while the VALU works on a result that has landed (three
+        // accumulator tiles rotate; at distance 1 the epilogue waits on the MFMA's latency);
+        // the last DEP MFMAs of a group are taken up under the first DEP of the next.  Operand reads fly two groups ahead.  Every group of the tile
         // is computed (rows past the causal end hold valid clamped keys; their scores are not
         // stored), so the fully unrolled sequence has no branches and the held slots,
         // accumulators and operand registers stay static.
         constexpr int NG = kIxTile / 16;
         constexpr int NK = 2 * NMT;
+        // epilogue distance in MFMAs: 2 needs three distinct accumulator tiles in a group
+        constexpr int DEP = NK >= 3 ? 2 : 1;
         v8i bq[2];
         v4f acc[2][NMT];
         float part[2][2];  // [group parity][token]
@@ -290,12 +293,11 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
                 const int tok = k / NMT, mt = k % NMT;
                 // MFMA k overwrites acc[k], whose previous contents were consumed a step ago
                 acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], bq[g & 1]);
-                if (k > 0) {
-                    epi_k(g, k - 1);
+                if (k >= DEP) {
+                    epi_k(g, k - DEP);
                 } else if (g > 0) {
-                    epi_k(g - 1, NK - 1);  // the previous group is complete
-                    if (g & 1) continue;
-                    reduce_pair(part[0], part[1], buf, (g - 1) >> 1);
+                    epi_k(g - 1, NK - DEP + k);  // the previous group's last DEP
+                    if (k == DEP - 1 && !(g & 1)) reduce_pair(part[0], part[1], buf, (g - 1) >> 1);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // the MFMA first,
                 __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then the FMAs
@@ -303,7 +305,8 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
             }
             if (g + 2 < NG) bq[g & 1] = load_b(buf, g + 2);
         }
-        epi_k(NG - 1, NK - 1);
+#pragma unroll
+        for (int d = DEP; d >= 1; --d) epi_k(NG - 1, NK - d);
         reduce_pair(part[0], part[1], buf, (NG - 1) >> 1);
         held_key0 = key0;
         held_groups = ngroups;
