@@ -375,3 +375,24 @@ def test_forward_decode_32_full_size_sampled(cuda):
     h = host_inputs(inp)
     for b in (0, 13, 31):
         compare_forward_rows(inp, h, out, lse, idx, [0], dims, f"decode32 seq {b}", seq=b)
+
+
+def test_forward_ragged_prefill_batch(cuda):
+    # three sequences in one call: a full prefill, a short one below k, and a chunk of 2500 new
+    # rows continuing a 9000-token cache (len_q < len_k); small workspace so passes split rows
+    dims = dsa_inputs.PROD
+    lq, lk = [3000, 700, 2500], [3000, 700, 9000]
+    say(f"forward prod ragged prefill batch lq {lq} lk {lk}")
+    parts = [dsa_inputs.prefill_inputs(n, dims, seed=20 + i, device=cuda) for i, n in enumerate(lk)]
+    inp = {"dims": dims}
+    for key in ("k8", "k_scale", "kv"):
+        inp[key] = torch.cat([p[key] for p in parts])
+    for key in ("q8", "q_scale", "w", "q"):
+        inp[key] = torch.cat([p[key][n - m:] for p, n, m in zip(parts, lk, lq)])
+    inp["cu_q"] = [0] + list(np.cumsum(lq))
+    inp["cu_k"] = [0] + list(np.cumsum(lk))
+    batch = dsa.Batch(inp["cu_q"], inp["cu_k"], device=cuda)
+    out, lse, idx = run_forward(inp, dims, cuda, ws_bytes=dsa.workspace_min(dims, batch) + (64 << 20))
+    h = host_inputs(inp)
+    for seq, rows in ((0, [0, 2047, 2048, 2999]), (1, [0, 350, 699]), (2, [0, 1, 1250, 2499])):
+        compare_forward_rows(inp, h, out, lse, idx, rows, dims, f"ragged seq {seq}", seq=seq)
