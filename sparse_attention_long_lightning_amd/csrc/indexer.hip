@@ -11,6 +11,15 @@
 //   instruction yields D_j for 16 heads x 16 keys.  Lane l holds key l%16 and heads
 //   4*(l/16)+r (r = 0..3) of the tile, so the weighted ReLU sum over heads runs inside the
 //   lane and needs only two cross-lane additions at the end.
+//
+// Linear part on the matrix cores (prefill): with ReLU(x) = (x + |x|) / 2,
+//     sum_j w'_j ReLU(D_j) = sum_j (w'_j/2) |D_j| + k8[s,:] . u,   u = sum_j (w'_j/2) q8[t,j,:]
+// The second term is linear in the key, so it is one more dot product per (t, s) instead of
+// one more FMA per head.  u (fp32, per token) is written as a sum of kLinTerms FP8 vectors
+// u = sum_i 2^(E-7-4i) c_i (E = exponent of max|u|; each term takes the rounding residual of
+// the ones before, |u - sum| <= 2^-4*kLinTerms * max|u|), and one extra MFMA per 16-key group,
+// whose A rows are the terms of the wave's two tokens, gives k8 . c_i for all of them.  The
+// epilogue is then one FMA per head instead of two.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -28,10 +37,35 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b) {
 __device__ __forceinline__ void materialize(const v8i& x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void materialize(float x) { asm volatile("" ::"v"(x)); }
 
-// The epilogues take p + w * ReLU(x) as two FMAs, w/2 * x and w/2 * |x|, using
+// The decode epilogue takes p + w * ReLU(x) as two FMAs, w/2 * x and w/2 * |x|, using
 // ReLU(x) = (x + |x|) / 2 with the 1/2 folded into w: max-based forms cost an extra
 // instruction to quiet the MFMA output first.  The two terms cancel to within fp32 rounding
-// of |w x| for x < 0, far below the FP8 products' own error.
+// of |w x| for x < 0, far below the FP8 products' own error.  (Prefill moves the x terms onto
+// the matrix cores, see above.)
+
+// x from the lane that DPP control CTRL names (row_mirror, row_half_mirror, quad_perm).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i within each row of 16
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within each half row
+constexpr int kDppQuadReverse = 0x1B;     // quad_perm [3,2,1,0]: i <-> i ^ 3
+constexpr int kDppQuadSwap = 0xB1;        // quad_perm [1,0,3,2]: i <-> i ^ 1
+
+// One reduce-scatter step over lane pairs (partners differ in the bit `upper`): each lane keeps
+// half of its 2N values (the upper half if `upper`) and adds the partner's copy of that half.
+template <int N, int CTRL>
+__device__ __forceinline__ void reduce_half(float* v, bool upper) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float keep = upper ? v[i + N] : v[i];
+        const float send = upper ? v[i] : v[i + N];
+        v[i] = keep + dpp_f<CTRL>(send);
+    }
+}
+
+constexpr int kLinTerms = 6;  // FP8 terms of the linear-part query (at most 8 rows per token)
 
 // Sum over the four 16-lane groups; every lane ends with the total of its column.
 __device__ __forceinline__ float sum_over_groups(float v) {
@@ -108,6 +142,7 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
     // all fly together instead of one branch-guarded round trip at a time.
     v8i qa[2][NMT];
     float wt[2][NMT][4];
+    float wa[2][NMT];  // w'/2 of the head of lane's A row (head mt*16 + col)
     int tpos[2];
     int trow[2];
 #pragma unroll
@@ -126,6 +161,11 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
             const v4i hi = *(const v4i*)(src + 16);
             const v8i a = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             qa[tok][mt] = qv ? a : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+            {
+                const int64_t e = qrow * H + min(h, H - 1);
+                const float v = 0.5f * w[e] * qs[e];
+                wa[tok][mt] = (ok && h < H) ? v : 0.f;
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int hh = mt * 16 + grp * 4 + r;
@@ -143,6 +183,7 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
             materialize(qa[tok][mt]);
+            materialize(wa[tok][mt]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) materialize(wt[tok][mt][r]);
         }
@@ -159,17 +200,21 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
     auto issue_tile = [&](int t) {
         const uint32_t buf = buf_of(t);
         const int key0 = seg0 + t * kIxTile;
+        // the per-lane offsets are recomputed for each tile (a few VALU) rather than kept
+        // live across the loop, where they would compete with the MFMA operands for registers
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int k = 0; k < T::PER_WAVE; ++k) {
             const int I = wv + kIxWaves * k;
             if (I < T::KEY_INSTRS) {
-                const int r = I * T::ROWS_PER_INSTR + lane / T::CH;
-                const int p = lane % T::CH;
+                const int r = I * T::ROWS_PER_INSTR + ln / T::CH;
+                const int p = ln % T::CH;
                 const int key = min(key0 + r, pmax);
                 dma16(kseq, (uint32_t)key * D + 16 * (p ^ T::swz(r)), buf + I * 1024);
             } else if (I < T::INSTRS) {
                 const int j = I - T::KEY_INSTRS;
-                const int key = min(key0 + 64 * j + lane, pmax);
+                const int key = min(key0 + 64 * j + ln, pmax);
                 dma4(sseq, (uint32_t)key * 4, buf + T::KEY_BYTES + 256 * j);
             }
         }
@@ -191,45 +236,124 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
     // its wait: stores issued between the direct loads would otherwise lengthen the waits
     // (they count on the same counter).  Slot s holds key groups 2s and 2s+1: lane group r
     // keeps group 2s + (r & 1) of token r >> 1, so each store instruction writes 64 scores.
+    // (Stores spread over the next tile's MFMA stream, one slot per group, measured slower.)
     float held[8];
     int held_key0 = 0, held_groups = 0;
-    auto flush = [&]() {
+    auto flush_slot = [&](int slot) {
         const int g_odd = grp & 1, tok = grp >> 1;
         const int my_pos = tok ? tpos[1] : tpos[0];
         const int64_t my_row = tok ? trow[1] : trow[0];
-#pragma unroll
-        for (int slot = 0; slot < 8; ++slot) {
-            const int g = 2 * slot + g_odd;
-            const int s = held_key0 + 16 * g + col;
-            if (g < held_groups && s <= my_pos) {
-                scores[my_row * stride + s] = held[slot];
-                if (hist != nullptr) {
-                    const uint32_t key = score_key(held[slot]);
-                    if (key >> 31) {
-                        const uint32_t b = (key >> 21) & (kHistBins - 1);
-                        atomicAdd(&hcount[2 * wv + tok][b >> 1], 1u << ((b & 1) << 4));
-                    }
+        const int g = 2 * slot + g_odd;
+        const int s = held_key0 + 16 * g + col;
+        if (g < held_groups && s <= my_pos) {
+            scores[my_row * stride + s] = held[slot];
+            if (hist != nullptr) {
+                const uint32_t key = score_key(held[slot]);
+                if (key >> 31) {
+                    const uint32_t b = (key >> 21) & (kHistBins - 1);
+                    atomicAdd(&hcount[2 * wv + tok][b >> 1], 1u << ((b & 1) << 4));
                 }
             }
         }
+    };
+    auto flush = [&]() {
+#pragma unroll
+        for (int slot = 0; slot < 8; ++slot) flush_slot(slot);
         held_groups = 0;
     };
     // Sums the partials of groups 2s (pe) and 2s+1 (po) over the four lane groups with two
     // lane-swap rounds, leaving lane group r with group 2s + (r & 1) of token r >> 1 (the
-    // layout flush expects), then applies that key's scale.
-    auto reduce_pair = [&](const float (&pe)[2], const float (&po)[2], uint32_t buf, int slot) {
+    // layout flush expects), then applies that key's scale (read a group ahead: a read here
+    // would make the MFMAs wait for every LDS read in flight, operand prefetch included).
+    auto reduce_pair = [&](const float (&pe)[2], const float (&po)[2], float kscale, int slot) {
         auto sw32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe[0]), __float_as_uint(pe[1]), false, false);
         auto sw32o = __builtin_amdgcn_permlane32_swap(__float_as_uint(po[0]), __float_as_uint(po[1]), false, false);
         const float x = __uint_as_float(sw32[0]) + __uint_as_float(sw32[1]);
         const float y = __uint_as_float(sw32o[0]) + __uint_as_float(sw32o[1]);
         auto sw16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
         const float z = __uint_as_float(sw16[0]) + __uint_as_float(sw16[1]);
-        const float kscale = *(const __attribute__((address_space(3))) float*)(size_t)(
-            buf + T::KEY_BYTES + 4 * (16 * (2 * slot + (grp & 1)) + col));
         held[slot] = z * kscale;
     };
     issue_tile(0);
     if (ntiles > 1) issue_tile(1);
+
+    // Linear-part query of each token, while the first tiles load.  u = sum_j (w'_j/2) q_j is
+    // folded in the A layout (lane: head mt*16 + col, dims 32*grp + e), summed over the 16 lanes
+    // of a row by a reduce-scatter that leaves dims 32*grp + 2*col + {0,1} in each lane, and
+    // split into FP8 terms there.  The codes go through LDS (ring buffer 2, not loaded before
+    // the first barrier of the tile loop) into the A fragment of the linear MFMA: row
+    // rho = col holds term rho & 7 of token rho >> 3 (terms >= kLinTerms are zero).
+    constexpr int kLinBytes = 2 * 8 * KGRP * 32;  // per wave: [token][term][K group][32 bytes]
+    static_assert(kIxBufs >= 3 && kIxWaves * kLinBytes <= T::BYTES, "linear codes fit ring buffer 2");
+    uint8_t* lin_lds = lds + 2 * T::BYTES + wv * kLinBytes;
+    v8i ql;
+    float lin_scale[2];  // multiplier of this lane's linear row sum for token 0 / 1
+    {
+        int ex[2];
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {
+            float v[32];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) v[e] = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int x = qa[tok][mt][i];
+                    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+                    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+                    v[4 * i + 0] = fmaf(wa[tok][mt], lo[0], v[4 * i + 0]);
+                    v[4 * i + 1] = fmaf(wa[tok][mt], lo[1], v[4 * i + 1]);
+                    v[4 * i + 2] = fmaf(wa[tok][mt], hi[0], v[4 * i + 2]);
+                    v[4 * i + 3] = fmaf(wa[tok][mt], hi[1], v[4 * i + 3]);
+                }
+            }
+            // partners of the four steps differ in lane bits 3, 2, 1, 0 of col (the masks
+            // 15, 7, 3, 1 generate every xor of the row, so all 16 lanes are summed)
+            reduce_half<16, kDppRowMirror>(v, col & 8);
+            reduce_half<8, kDppRowHalfMirror>(v, col & 4);
+            reduce_half<4, kDppQuadReverse>(v, col & 2);
+            reduce_half<2, kDppQuadSwap>(v, col & 1);
+            float m = fmaxf(fabsf(v[0]), fabsf(v[1]));
+            m = fmaxf(m, dpp_f<kDppRowMirror>(m));
+            m = fmaxf(m, dpp_f<kDppRowHalfMirror>(m));
+            m = fmaxf(m, dpp_f<kDppQuadReverse>(m));
+            m = fmaxf(m, dpp_f<kDppQuadSwap>(m));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            // E = exponent of max|u| (at least -100, so every scale below is a normal float or
+            // an exact subnormal); |u| < 2^(E+1) puts the first term below 256, and each
+            // residual is at most half an FP8 step of the term before, below 128 in the next
+            // term's units, so no term saturates.
+            const int e = max((int)((__float_as_uint(m) >> 23) & 0xff) - 127, -100);
+            ex[tok] = __builtin_amdgcn_readfirstlane(e);
+#pragma unroll
+            for (int j = 0; j < kLinTerms; ++j) {
+                const float up = ldexpf(1.f, 7 + 4 * j - ex[tok]);
+                const float dn = ldexpf(1.f, ex[tok] - 7 - 4 * j);
+                const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * up, v[1] * up, 0, false);
+                const auto back = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+                v[0] = fmaf(-back[0], dn, v[0]);  // exact: the rounding residual
+                v[1] = fmaf(-back[1], dn, v[1]);
+                if (grp < KGRP)
+                    *(uint16_t*)(lin_lds + ((tok * 8 + j) * KGRP + grp) * 32 + 2 * col) = (uint16_t)pk;
+            }
+        }
+        const int rt = col >> 3, rj = col & 7;
+        const uint8_t* src = lin_lds + ((rt * 8 + min(rj, kLinTerms - 1)) * KGRP + min(grp, KGRP - 1)) * 32;
+        const v4i lo = *(const v4i*)src;
+        const v4i hi = *(const v4i*)(src + 16);
+        ql = (rj < kLinTerms && grp < KGRP) ? (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}
+                                            : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+        materialize(ql);  // the reads complete before the buffer is reused
+        // C layout of the linear MFMA: lane group grp holds rows 4*grp + r, i.e. terms
+        // 4*(grp & 1) + r of token grp >> 1, whose sum is 2^(E-7-16*(grp&1)) * (C0 + C1/16 +
+        // C2/256 + C3/4096)
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok)
+            lin_scale[tok] = (grp >> 1) == tok ? ldexpf(1.f, ex[tok] - 7 - 16 * (grp & 1)) : 0.f;
+    }
+
     for (int t = 0; t < ntiles; ++t) {
         // Tile t has landed for this wave (the younger loads of tile t+1 may still fly; the
         // stores issued since are older than nothing we wait for), then for every wave; the
@@ -252,52 +376,70 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         const uint32_t buf = buf_of(t);
         const int ngroups = min(kIxTile / 16, (tmax - key0) / 16 + 1);
 
-        // The eight MFMAs of a group (token-major: k = 4*tok + mt) each run with the epilogue
-        // FMAs of the MFMA issued DEP = 2 before them (1 with two MFMAs per group), so the
-        // matrix pipe stays busy while the VALU works on a result that has landed (three
-        // accumulator tiles rotate; at distance 1 the epilogue waits on the MFMA's latency);
-        // the last DEP MFMAs of a group are taken up under the first DEP of the next.  Operand reads fly two groups ahead.  Every group of the tile
-        // is computed (rows past the causal end hold valid clamped keys; their scores are not
-        // stored), so the fully unrolled sequence has no branches and the held slots,
-        // accumulators and operand registers stay static.
+        // The MFMAs of a group (k = 0: the linear part of both tokens; then token-major,
+        // k = 1 + NMT*tok + mt) each run with the epilogue of the MFMA issued DEP = 2 before
+        // them, so the matrix pipe stays busy while the VALU works on a result that has landed
+        // (three accumulator tiles rotate; at distance 1 the epilogue would wait on the MFMA's
+        // latency); the last DEP MFMAs of a group are taken up under the first DEP of the next.
+        // Operand reads fly two groups ahead.  Every group of the tile is computed (rows past
+        // the causal end hold valid clamped keys; their scores are not stored), so the fully
+        // unrolled sequence has no branches and the held slots, accumulators and operand
+        // registers stay static.
         constexpr int NG = kIxTile / 16;
-        constexpr int NK = 2 * NMT;
-        // epilogue distance in MFMAs: 2 needs three distinct accumulator tiles in a group
-        constexpr int DEP = NK >= 3 ? 2 : 1;
+        constexpr int NK = 2 * NMT + 1;
+        constexpr int DEP = 2;
         v8i bq[2];
         v4f acc[2][NMT];
+        v4f accl;
         float part[2][2];  // [group parity][token]
         bq[0] = load_b(buf, 0);
         bq[1] = load_b(buf, 1);
-        // Epilogue FMAs of MFMA k of group gg, as two independent chains (the x terms and the
-        // |x| terms) so consecutive FMAs do not wait on each other.
-        float lin[2][2], mag[2][2];  // [group parity][token]
+        // Epilogue of MFMA k of group gg.  The linear MFMA's row sum starts each token's chain
+        // of |x| terms (dependent VALU instructions issue back to back at the wave's cadence).
+        float linv[2][2], ev[2][2];  // [group parity][token]
+        float kscale = 0.f;  // scale of this lane's key in the next slot to be reduced
         auto epi_k = [&](int gg, int k) {
-            const int tok = k / NMT, mt = k % NMT;
-            float a = mt == 0 ? 0.f : lin[gg & 1][tok];
-            float m = mt == 0 ? 0.f : mag[gg & 1][tok];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                a = fmaf(wt[tok][mt][r], acc[tok][mt][r], a);
-                m = fmaf(wt[tok][mt][r], fabsf(acc[tok][mt][r]), m);
+            if (k == 0) {
+                float hs = fmaf(accl[3], 0.0625f, accl[2]);
+                hs = fmaf(hs, 0.0625f, accl[1]);
+                hs = fmaf(hs, 0.0625f, accl[0]);
+                float l0 = hs * lin_scale[0], l1 = hs * lin_scale[1];
+                asm volatile("" : "+v"(l0), "+v"(l1));
+                linv[gg & 1][0] = l0;
+                linv[gg & 1][1] = l1;
+                return;
             }
-            asm volatile("" : "+v"(a), "+v"(m));  // keep these FMAs in this step
-            lin[gg & 1][tok] = a;
-            mag[gg & 1][tok] = m;
-            if (mt == NMT - 1) part[gg & 1][tok] = a + m;
+            const int tok = (k - 1) / NMT, mt = (k - 1) % NMT;
+            float a = mt == 0 ? linv[gg & 1][tok] : ev[gg & 1][tok];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a = fmaf(wt[tok][mt][r], fabsf(acc[tok][mt][r]), a);
+            asm volatile("" : "+v"(a));  // keep these FMAs in this step
+            ev[gg & 1][tok] = a;
+            if (mt == NMT - 1) part[gg & 1][tok] = a;
         };
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
 #pragma unroll
             for (int k = 0; k < NK; ++k) {
-                const int tok = k / NMT, mt = k % NMT;
-                // MFMA k overwrites acc[k], whose previous contents were consumed a step ago
-                acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], bq[g & 1]);
+                // MFMA k overwrites its accumulator, whose previous contents were consumed a
+                // step ago
+                if (k == 0) {
+                    if (g & 1) {  // slot (g-1)/2 holds groups g-1 and g; lane group r keeps g-1+(r&1)
+                        int ln = lane;  // recomputed, not held in a register per group
+                        asm volatile("" : "+v"(ln));
+                        kscale = *(const __attribute__((address_space(3))) float*)(size_t)(
+                            buf + T::KEY_BYTES + 4 * (16 * (g - 1 + ((ln >> 4) & 1)) + (ln & 15)));
+                    }
+                    accl = mfma_fp8_16x16x128(ql, bq[g & 1]);
+                } else {
+                    const int tok = (k - 1) / NMT, mt = (k - 1) % NMT;
+                    acc[tok][mt] = mfma_fp8_16x16x128(qa[tok][mt], bq[g & 1]);
+                }
                 if (k >= DEP) {
                     epi_k(g, k - DEP);
                 } else if (g > 0) {
                     epi_k(g - 1, NK - DEP + k);  // the previous group's last DEP
-                    if (k == DEP - 1 && !(g & 1)) reduce_pair(part[0], part[1], buf, (g - 1) >> 1);
+                    if (k == DEP - 1 && !(g & 1)) reduce_pair(part[0], part[1], kscale, (g - 1) >> 1);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // the MFMA first,
                 __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then the FMAs
@@ -307,7 +449,7 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         }
 #pragma unroll
         for (int d = DEP; d >= 1; --d) epi_k(NG - 1, NK - d);
-        reduce_pair(part[0], part[1], buf, (NG - 1) >> 1);
+        reduce_pair(part[0], part[1], kscale, (NG - 1) >> 1);
         held_key0 = key0;
         held_groups = ngroups;
     }
