@@ -239,6 +239,13 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
     // (Stores spread over the next tile's MFMA stream, one slot per group, measured slower.)
     float held[8];
     int held_key0 = 0, held_groups = 0;
+    // Counts a stored score if it is >= +0 (the top bit of its order-preserving key is set):
+    // for such scores key bits 30..21 are the float's own bits 30..21 (-0 counts as +0 in
+    // bin 0; NaN and negative scores fail the comparison).
+    auto count = [&](float v, int tok) {
+        const uint32_t b = (__float_as_uint(v) >> 21) & (kHistBins - 1);
+        if (v >= 0.f) atomicAdd(&hcount[2 * wv + tok][b >> 1], 1u << ((b & 1) << 4));
+    };
     auto flush_slot = [&](int slot) {
         const int g_odd = grp & 1, tok = grp >> 1;
         const int my_pos = tok ? tpos[1] : tpos[0];
@@ -247,18 +254,23 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_prefill_kernel(
         const int s = held_key0 + 16 * g + col;
         if (g < held_groups && s <= my_pos) {
             scores[my_row * stride + s] = held[slot];
-            if (hist != nullptr) {
-                const uint32_t key = score_key(held[slot]);
-                if (key >> 31) {
-                    const uint32_t b = (key >> 21) & (kHistBins - 1);
-                    atomicAdd(&hcount[2 * wv + tok][b >> 1], 1u << ((b & 1) << 4));
-                }
-            }
+            if (hist != nullptr) count(held[slot], tok);
         }
     };
     auto flush = [&]() {
+        if (held_groups == kIxTile / 16 && held_key0 + kIxTile - 1 <= min(tpos[0], tpos[1])) {
+            // the whole held tile lies below both tokens' positions: no per-slot tests
+            const int tok = grp >> 1;
+            float* rp = scores + (int64_t)(tok ? trow[1] : trow[0]) * stride + held_key0 + 16 * (grp & 1) + col;
 #pragma unroll
-        for (int slot = 0; slot < 8; ++slot) flush_slot(slot);
+            for (int slot = 0; slot < 8; ++slot) {
+                rp[32 * slot] = held[slot];
+                if (hist != nullptr) count(held[slot], tok);
+            }
+        } else {
+#pragma unroll
+            for (int slot = 0; slot < 8; ++slot) flush_slot(slot);
+        }
         held_groups = 0;
     };
     // Sums the partials of groups 2s (pe) and 2s+1 (po) over the four lane groups with two

@@ -82,6 +82,34 @@ def test_indexer_prod_ragged_all_rows(cuda):
     compare_indexer_rows(scores, host_inputs(inp), np.arange(1100), "prod-1100")
 
 
+@pytest.mark.parametrize("dims_name,L", [("prod", 700), ("tiny", 300)])
+def test_indexer_head_weight_extremes(cuda, dims_name, L):
+    # The prefill kernel computes the linear half of w * ReLU(x) = w/2 * (x + |x|) as one dot
+    # product with u = sum_j w'_j/2 q_j, expanded in FP8 terms scaled by the exponent of
+    # max|u|.  Rows cycle through weights of tiny and huge magnitude, all zero (u = 0), a single
+    # head, magnitudes spread over twelve decades with alternating signs, and all negative.
+    dims = dsa_inputs.PROD if dims_name == "prod" else dsa_inputs.TINY
+    say(f"indexer {dims_name} L={L}, extreme head weights")
+    inp = dsa_inputs.prefill_inputs(L, dims, seed=4, device=cuda, needles=False)
+    H = dims.n_idx_heads
+    w = inp["w"].clone()
+    kind = torch.arange(L, device=cuda) % 6
+    j = torch.arange(H, device=cuda)
+    spread = torch.where(j % 2 == 0, 1.0, -1.0) * torch.pow(10.0, (j % 12 - 6).float())
+    one = torch.zeros(H, device=cuda)
+    one[H // 3] = 1.7
+    w[kind == 0] *= 1e-33
+    w[kind == 1] *= 1e25
+    w[kind == 2] = 0.0
+    w[kind == 3] = one
+    w[kind == 4] = spread
+    w[kind == 5] = -w[kind == 5].abs()
+    inp["w"] = w.contiguous()
+    scores = host(run_indexer(inp, dims, cuda))
+    compare_indexer_rows(scores, host_inputs(inp), np.arange(L), f"{dims_name} weight extremes")
+    assert np.all(scores[2::6][np.isfinite(scores[2::6])] == 0.0)
+
+
 def test_indexer_prod_16k_sampled_rows(cuda):
     say("indexer prod L=16384 sampled rows")
     dims = dsa_inputs.PROD
