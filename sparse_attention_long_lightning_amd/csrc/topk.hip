@@ -796,41 +796,86 @@ __global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __r
         return;
     }
     // ---- one pass: every element of digit >= b1 into the list ----
+    // Here b1 >= kHistBins (the threshold lies among the scores >= +0, below +inf's digit), and
+    // for such digits key >> 21 >= b1 holds exactly when x >= thr, the float whose bits are
+    // (b1 - kHistBins) << 21: non-negative floats order like their bits, -0 passes only when
+    // thr = +0 (its key digit is kHistBins), negative scores and NaN never pass.  So the scan
+    // is one float compare per element; the keys are formed for the few that pass, which are
+    // placed by wave ballots (the list order is free).
+    const float thr = __uint_as_float((uint32_t)(b1 - kHistBins) << 21);
     if (tid == 0) sm.count = 0;
     __syncthreads();
     const int seg = ((n + kWaves - 1) / kWaves + 255) & ~255;
     const int sb = min(n, wv * seg), se = min(n, sb + seg);
-    for (int e0 = sb; e0 < se; e0 += 256 * kUnroll) {
-        uint32_t k[kUnroll][4];
-        bool ok[kUnroll][4];
+    constexpr int kStep = 256 * kUnroll;
+    // loads of one step: whole steps need no bounds checks
+    auto load_step = [&](int e0, bool whole, float (&v)[kUnroll][4]) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) load4(x, e0 + 256 * u + 4 * lane, se, k[u], ok[u]);
-        int f = 0;
+        for (int u = 0; u < kUnroll; ++u) {
+            const int e = e0 + 256 * u + 4 * lane;
+            if (whole || e + 3 < se) {
+                const float4 t = *(const float4*)(x + e);
+                v[u][0] = t.x;
+                v[u][1] = t.y;
+                v[u][2] = t.z;
+                v[u][3] = t.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[u][c] = e + c < se ? x[e + c] : -INFINITY;
+            }
+        }
+    };
+    auto append_step = [&](int e0, const float (&v)[kUnroll][4]) {
+        uint64_t m[kUnroll][4];
+        int tot = 0;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                ok[u][c] = ok[u][c] && (int)(k[u][c] >> 21) >= b1;
-                f += ok[u][c];
+                m[u][c] = __ballot(v[u][c] >= thr);
+                tot += __popcll(m[u][c]);
             }
-        int wtot;
-        const int excl = wave_slot(f, wtot);
-        if (wtot == 0) continue;
+        if (tot == 0) return;
         int base = 0;
-        if (lane == 0) base = atomicAdd(&sm.count, wtot);
-        base = __shfl(base, 0);
-        int j = base + excl;
+        if (lane == 0) base = atomicAdd(&sm.count, tot);
+        base = __builtin_amdgcn_readfirstlane(__shfl(base, 0));
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (ok[u][c]) {
+            for (int c = 0; c < 4; ++c) {
+                const uint64_t mk = m[u][c];
+                if (mk == 0) continue;
+                if ((mk >> lane) & 1) {
+                    const int j = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
                     if (j < kCap) {
-                        sm.key[j] = k[u][c];
+                        sm.key[j] = score_key(v[u][c]);
                         sm.pos[j] = e0 + 256 * u + 4 * lane + c;
                     }
-                    ++j;
                 }
+                base += __popcll(mk);
+            }
+    };
+    // Whole steps alternate between two register sets, the next step's loads in flight while
+    // this one is appended (loads are unconditional, the last step re-read if needed, so the
+    // wait before each append is for the older set only); then the tail.
+    const int nsteps = (se - sb) / kStep;
+    int e0 = sb + nsteps * kStep;
+    if (nsteps > 0) {
+        float va[kUnroll][4], vb[kUnroll][4];
+        load_step(sb, true, va);
+        for (int i = 0; i < nsteps; i += 2) {
+            load_step(sb + min(i + 1, nsteps - 1) * kStep, true, vb);
+            append_step(sb + i * kStep, va);
+            if (i + 1 >= nsteps) break;
+            load_step(sb + min(i + 2, nsteps - 1) * kStep, true, va);
+            append_step(sb + (i + 1) * kStep, vb);
+        }
+    }
+    if (e0 < se) {
+        float v[kUnroll][4];
+        load_step(e0, false, v);
+        append_step(e0, v);
     }
     __syncthreads();
     finish_from_list(sm, nlist, topk, n, out);
