@@ -112,8 +112,8 @@ struct ForwardPlan {
 
 // Workspace layout of dsa_forward: [scores | idx (when idx_out is NULL) | hist | tail].
 // Prefill: hist holds the indexer's per-row score counts that the top-k starts from.
-// Decode: the tail holds the top-k candidates and, later on the same stream, the MQA split
-// partials.
+// Decode: the tail holds the per-row score counts, the top-k list sizes and lists, and,
+// later on the same stream, the MQA split partials.
 ForwardPlan plan_forward(const dsa_dims* d, Shape shape, const Batch& bt, int chunk) {
     ForwardPlan p;
     p.stride = score_stride_for(bt);
@@ -123,7 +123,7 @@ ForwardPlan plan_forward(const dsa_dims* d, Shape shape, const Batch& bt, int ch
     p.hist_off = p.idx_off + align_up((size_t)p.chunk * d->topk * sizeof(int32_t));
     const size_t hist_bytes = bt.decode ? 0 : (size_t)p.chunk * kHistBins * sizeof(uint32_t);
     p.tail_off = p.hist_off + align_up(hist_bytes);
-    p.topk_bytes = bt.decode ? topk_ws_bytes(p.chunk, bt.max_lk, d->topk) : 0;
+    p.topk_bytes = bt.decode ? (size_t)p.chunk * kHistBins * sizeof(uint32_t) + topk_list_ws_bytes(p.chunk) : 0;
     size_t tail = p.topk_bytes;
     if (bt.decode) {
         const size_t mqa = mqa_split_bytes(shape, bt.T, mqa_splits(bt.T, d->topk));
@@ -354,10 +354,15 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
         if (debug_log())
             fprintf(stderr, "[dsa] decode B=%d max_len_k=%d stride=%lld splits=%d\n", bt.B, bt.max_lk,
                     (long long)p.stride, n_split);
-        hipError_t e = launch_indexer_decode(ia, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, bt.pages,
-                                             bt.pages_per_seq, stream);
+        // tail: [counts (T x kHistBins) | list sizes (T) | lists]; counts and sizes start at 0
+        uint32_t* hs = (uint32_t*)(wsb + p.tail_off);
+        hipError_t e = launch_zero_words(hs, (int64_t)bt.T * (kHistBins + 1), stream);
         if (e == hipSuccess)
-            e = launch_topk(sc, p.stride, ix, topk, map, bt.T, bt.max_lk, wsb + p.tail_off, p.topk_bytes, stream);
+            e = launch_indexer_decode(ia, bt.B, bt.max_lk, batch->cu_q_dev, batch->cu_k_dev, bt.pages,
+                                      bt.pages_per_seq, stream, hs);
+        if (e == hipSuccess)
+            e = launch_topk_list(sc, p.stride, hs, ix, topk, map, bt.T, bt.max_lk, hs + (size_t)bt.T * kHistBins,
+                                 stream);
         if (e == hipSuccess) e = launch_sparse_mqa(ma, map, bt.T, n_split, wsb + p.tail_off, stream);
         return hip_status(e);
     }

@@ -495,9 +495,11 @@ __global__ __launch_bounds__(kDecodeThreads) void indexer_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, float* __restrict__ scores,
     int64_t stride, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-    const int32_t* __restrict__ pages, int pages_per_seq) {
+    const int32_t* __restrict__ pages, int pages_per_seq, uint32_t* __restrict__ hist) {
     constexpr int NMT = (H + 15) / 16;
     constexpr int KGRP = D / 32;
+    // counts of this workgroup's stored scores >= +0 by key bits 30..21 (when hist is given)
+    __shared__ uint32_t hcount[kHistBins];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -507,9 +509,15 @@ __global__ __launch_bounds__(kDecodeThreads) void indexer_decode_kernel(
     const int kbase = cu_k[b];
     const int nkeys = cu_k[b + 1] - kbase;
     const int qrow = cu_q[b];  // decode: exactly one query row, at position nkeys - 1
+    if (blockIdx.x * kDecodeKeys >= nkeys) return;  // the whole workgroup
+    if (hist != nullptr) {
+        for (int j = tid; j < kHistBins; j += kDecodeThreads) hcount[j] = 0u;
+        __syncthreads();
+    }
     const int s_begin = blockIdx.x * kDecodeKeys + wv * kDecodeKeysPerWave;
-    if (s_begin >= nkeys) return;
-    const int s_end = min(s_begin + kDecodeKeysPerWave, nkeys);
+    // a wave past the keys takes part in the barriers only
+    const int s_end = max(s_begin, min(s_begin + kDecodeKeysPerWave, nkeys));
+    if (s_begin < s_end) {
 
     v8i qa[NMT];
     float wt[NMT][4];  // half the folded weight: w * ReLU(x) = wt * x + wt * |x|
@@ -591,7 +599,21 @@ __global__ __launch_bounds__(kDecodeThreads) void indexer_decode_kernel(
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
         const int s = s_begin + st * STEP + 16 * grp + col;
-        if (s < s_end) srow[s] = held[st];
+        if (s < s_end) {
+            srow[s] = held[st];
+            // a score >= +0 has key bits 30..21 equal to its own bits 30..21 (-0 in bin 0)
+            const uint32_t bin = (__float_as_uint(held[st]) >> 21) & (kHistBins - 1);
+            if (hist != nullptr && held[st] >= 0.f) atomicAdd(&hcount[bin], 1u);
+        }
+    }
+    }  // s_begin < s_end
+    if (hist != nullptr) {
+        __syncthreads();
+        uint32_t* hrow = hist + (int64_t)qrow * kHistBins;
+        for (int j = tid; j < kHistBins; j += kDecodeThreads) {
+            const uint32_t c = hcount[j];
+            if (c != 0u) atomicAdd(&hrow[j], c);
+        }
     }
 }
 
@@ -609,11 +631,12 @@ hipError_t launch_prefill_t(const IndexerArgs& a, int row0, int n_rows, int pos0
 
 template <int H, int D>
 hipError_t launch_decode_t(const IndexerArgs& a, int n_seqs, int max_keys, const int32_t* cu_q,
-                           const int32_t* cu_k, const int32_t* pages, int pages_per_seq, hipStream_t st) {
+                           const int32_t* cu_k, const int32_t* pages, int pages_per_seq, uint32_t* hist,
+                           hipStream_t st) {
     dim3 grid((max_keys + kDecodeKeys - 1) / kDecodeKeys, n_seqs);
     hipLaunchKernelGGL((indexer_decode_kernel<H, D>), grid, dim3(kDecodeThreads), 0, st, a.q8,
                        a.q_scale, a.w, a.k8, a.k_scale, a.scores, a.score_stride, cu_q, cu_k, pages,
-                       pages_per_seq);
+                       pages_per_seq, hist);
     return hipGetLastError();
 }
 
@@ -627,10 +650,10 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a, int row0, int n_rows, in
 
 hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,
                                  const int32_t* cu_q, const int32_t* cu_k, const int32_t* pages,
-                                 int pages_per_seq, hipStream_t st) {
+                                 int pages_per_seq, hipStream_t st, uint32_t* hist) {
     if (a.shape == Shape::Prod)
-        return launch_decode_t<64, 128>(a, n_seqs, max_keys, cu_q, cu_k, pages, pages_per_seq, st);
-    return launch_decode_t<4, 32>(a, n_seqs, max_keys, cu_q, cu_k, pages, pages_per_seq, st);
+        return launch_decode_t<64, 128>(a, n_seqs, max_keys, cu_q, cu_k, pages, pages_per_seq, hist, st);
+    return launch_decode_t<4, 32>(a, n_seqs, max_keys, cu_q, cu_k, pages, pages_per_seq, hist, st);
 }
 
 }  // namespace dsa

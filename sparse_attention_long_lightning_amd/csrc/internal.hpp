@@ -31,15 +31,25 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a, int row0, int n_rows, in
                                   int kbase, float* scores, hipStream_t st, uint32_t* hist = nullptr);
 // Decode: one query row per sequence (cu_q[b+1] - cu_q[b] == 1); row cu_q[b] of the scores.
 // Paged caches: pages != nullptr (see RowMap).
+// With hist, also adds each row's counts of stored scores >= +0 by key bits 30..21 to
+// hist + row * kHistBins (which must start at 0), like the prefill kernel.
 hipError_t launch_indexer_decode(const IndexerArgs& a, int n_seqs, int max_keys,
                                  const int32_t* cu_q, const int32_t* cu_k, const int32_t* pages,
-                                 int pages_per_seq, hipStream_t st);
+                                 int pages_per_seq, hipStream_t st, uint32_t* hist = nullptr);
 
 // Top-k over n_rows score rows; row i reads scores + i * stride and writes idx + i * topk.
 // With a workspace of topk_ws_bytes(n_rows, max_len, topk) bytes (max_len = the longest
 // row) rows are split over several workgroups; without one (or for rows too long for the
 // split) one workgroup selects each row.  Both give the same result.
 size_t topk_ws_bytes(int n_rows, int max_len, int topk);
+// Top-k of few long rows from the indexer's per-row counts (decode): segment workgroups
+// append each row's candidates to a list in the workspace, then one workgroup per row selects
+// from it; rows the list path does not apply to are selected from the scores.  The workspace
+// holds topk_list_ws_bytes(n_rows) bytes: n_rows int list sizes, which must be 0 at the
+// launch, then the lists.  The result equals launch_topk's.
+size_t topk_list_ws_bytes(int n_rows);
+hipError_t launch_topk_list(const float* scores, int64_t stride, const uint32_t* hist, int32_t* idx, int topk,
+                            const RowMap& map, int n_rows, int max_len, void* ws, hipStream_t st);
 // Top-k of rows whose non-negative scores the indexer counted into hist (kHistBins per row):
 // one read of each row when it holds at least topk non-negative scores; the same result.
 hipError_t launch_topk_from_hist(const float* scores, int64_t stride, const uint32_t* hist, int32_t* idx,

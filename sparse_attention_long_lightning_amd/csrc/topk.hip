@@ -749,28 +749,33 @@ __device__ void finish_from_list(FusedSmem& sm, int nlist, int topk, int n, int3
 // The first digit from a row's counts: the threshold digit b1 and the number of elements of
 // digit >= b1; false when the list path does not apply (fewer than topk counted scores, more
 // than kCap candidates, or a row longer than the bitmaps).  Ends with a barrier.
-__device__ bool threshold_from_counts(FusedSmem& sm, const uint32_t* __restrict__ h, int n, int topk, int& b1,
+__device__ bool threshold_from_counts(SelSmem& sel, const uint32_t* __restrict__ h, int n, int topk, int& b1,
                                       int& nlist) {
     int cnt = 0;
     for (int b = threadIdx.x; b < kHistBins; b += kThreads) {
         const uint32_t c = h[b];
-        sm.sel.hist[b] = c;
+        sel.hist[b] = c;
         cnt += (int)c;
     }
     int total;
-    block_exclusive_scan(cnt, sm.sel.wsum, total);  // also orders the histogram writes
+    block_exclusive_scan(cnt, sel.wsum, total);  // also orders the histogram writes
     bool fused = total >= topk && n <= kFusedMaxLen;
     b1 = 0;
     nlist = 0;
     if (fused) {
-        find_threshold(sm.sel.hist, kHistBins, topk, sm.sel);
-        b1 = kHistBins + sm.sel.sel_bin;
-        nlist = sm.sel.sel_above + (int)sm.sel.hist[sm.sel.sel_bin];
+        find_threshold(sel.hist, kHistBins, topk, sel);
+        b1 = kHistBins + sel.sel_bin;
+        nlist = sel.sel_above + (int)sel.hist[sel.sel_bin];
         fused = nlist <= kCap;
     }
     __syncthreads();  // every thread has read the threshold before the shared memory is reused
     return fused;
 }
+
+// The float whose bits are (b1 - kHistBins) << 21: for a threshold digit b1 among the scores
+// >= +0 (b1 >= kHistBins, at most +inf's digit), an element's key digit is >= b1 exactly when
+// the element compares >= this float (see topk_hist_kernel).
+__device__ __forceinline__ float list_threshold(int b1) { return __uint_as_float((uint32_t)(b1 - kHistBins) << 21); }
 
 __global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __restrict__ scores, int64_t stride,
                                                                 const uint32_t* __restrict__ hist,
@@ -790,7 +795,7 @@ __global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __r
     }
     const float* x = scores + (int64_t)row * stride;
     int b1, nlist;
-    const bool fused = threshold_from_counts(sm, hist + (int64_t)row * kHistBins, n, topk, b1, nlist);
+    const bool fused = threshold_from_counts(sm.sel, hist + (int64_t)row * kHistBins, n, topk, b1, nlist);
     if (!fused) {
         select_row(smu.full, x, n, topk, out);
         return;
@@ -802,7 +807,7 @@ __global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __r
     // thr = +0 (its key digit is kHistBins), negative scores and NaN never pass.  So the scan
     // is one float compare per element; the keys are formed for the few that pass, which are
     // placed by wave ballots (the list order is free).
-    const float thr = __uint_as_float((uint32_t)(b1 - kHistBins) << 21);
+    const float thr = list_threshold(b1);
     if (tid == 0) sm.count = 0;
     __syncthreads();
     const int seg = ((n + kWaves - 1) / kWaves + 255) & ~255;
@@ -881,7 +886,170 @@ __global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __r
     finish_from_list(sm, nlist, topk, n, out);
 }
 
+// Few long rows (decode): the list path split over segment workgroups.  Every workgroup of a
+// row finds the row's threshold digit from the counts and appends the elements of its kSeg
+// scores that reach it to the row's list in global memory (in any order, one global atomic
+// per workgroup); topk_list_finish_kernel then selects from the list with one workgroup
+// per row.  A row the list path does not apply to is left to the finish kernel's select_row.
+__global__ __launch_bounds__(kThreads, 2) void topk_list_append_kernel(const float* __restrict__ scores,
+                                                                       int64_t stride,
+                                                                       const uint32_t* __restrict__ hist,
+                                                                       int topk, RowMap map, int n_rows,
+                                                                       uint32_t* __restrict__ lkey,
+                                                                       int32_t* __restrict__ lpos,
+                                                                       int* __restrict__ lcount) {
+    __shared__ SelSmem sel;
+    const int row = blockIdx.y;
+    if (row >= n_rows) return;
+    const int n = row_info(map, row).pos + 1;
+    const int s0 = blockIdx.x * kSeg;
+    if (n <= topk || s0 >= n) return;
+    int b1, nlist;
+    if (!threshold_from_counts(sel, hist + (int64_t)row * kHistBins, n, topk, b1, nlist)) return;
+    const float thr = list_threshold(b1);
+    const float* x = scores + (int64_t)row * stride;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    constexpr int kPerWave = kSeg / kWaves;  // whole steps of 256 * kUnroll elements
+    constexpr int kSteps = kPerWave / (256 * kUnroll);
+    static_assert(kPerWave % (256 * kUnroll) == 0, "whole steps per wave");
+    const int sb = min(n, s0 + wv * kPerWave), se = min(n, sb + kPerWave);
+    // the wave's scores stay in registers: they are counted first, so that the workgroup
+    // reserves its list space with one atomic (atomics of many waves on one row's counter
+    // serialize), then placed
+    float v[kSteps][kUnroll][4];
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int e = sb + 256 * (kUnroll * st + u) + 4 * lane;
+            if (e + 3 < se) {
+                const float4 t = *(const float4*)(x + e);
+                v[st][u][0] = t.x;
+                v[st][u][1] = t.y;
+                v[st][u][2] = t.z;
+                v[st][u][3] = t.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[st][u][c] = e + c < se ? x[e + c] : -INFINITY;
+            }
+        }
+    int cnt = 0;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cnt += __popcll(__ballot(v[st][u][c] >= thr));
+    __shared__ int wave_cnt[kWaves];
+    __shared__ int wg_base;
+    if (lane == 0) wave_cnt[wv] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int tot = 0;
+        for (int w = 0; w < kWaves; ++w) tot += wave_cnt[w];
+        wg_base = tot > 0 ? atomicAdd(&lcount[row], tot) : 0;
+    }
+    __syncthreads();
+    if (cnt == 0) return;
+    int base = wg_base;
+    for (int w = 0; w < wv; ++w) base += wave_cnt[w];
+    base = __builtin_amdgcn_readfirstlane(base);
+    uint32_t* rkey = lkey + (int64_t)row * kCap;
+    int32_t* rpos = lpos + (int64_t)row * kCap;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool pass = v[st][u][c] >= thr;
+                const uint64_t mk = __ballot(pass);
+                if (mk == 0) continue;
+                if (pass) {
+                    const int j = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+                    if (j < kCap) {  // the counts bound the list by nlist <= kCap
+                        rkey[j] = score_key(v[st][u][c]);
+                        rpos[j] = sb + 256 * (kUnroll * st + u) + 4 * lane + c;
+                    }
+                }
+                base += __popcll(mk);
+            }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void topk_list_finish_kernel(const float* __restrict__ scores,
+                                                                       int64_t stride,
+                                                                       const uint32_t* __restrict__ hist,
+                                                                       int32_t* __restrict__ idx, int topk,
+                                                                       RowMap map, int n_rows,
+                                                                       const uint32_t* __restrict__ lkey,
+                                                                       const int32_t* __restrict__ lpos) {
+    __shared__ __attribute__((aligned(16))) TopkSmem smu;
+    FusedSmem& sm = smu.fused;
+    const int row = blockIdx.x;
+    if (row >= n_rows) return;
+    const int n = row_info(map, row).pos + 1;
+    int32_t* out = idx + (int64_t)row * topk;
+    const int tid = threadIdx.x;
+    if (n <= topk) {
+        for (int j = tid; j < topk; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    const float* x = scores + (int64_t)row * stride;
+    int b1, nlist;
+    if (!threshold_from_counts(sm.sel, hist + (int64_t)row * kHistBins, n, topk, b1, nlist)) {
+        select_row(smu.full, x, n, topk, out);
+        return;
+    }
+    // every load of the list is issued before the first is used (a plain loop would wait for
+    // each round trip in turn)
+    constexpr int kPer = kCap / kThreads;
+    uint32_t kk[kPer];
+    int32_t pp[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int j = tid + i * kThreads;
+        if (j < nlist) {
+            kk[i] = lkey[(int64_t)row * kCap + j];
+            pp[i] = lpos[(int64_t)row * kCap + j];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int j = tid + i * kThreads;
+        if (j < nlist) {
+            sm.key[j] = kk[i];
+            sm.pos[j] = pp[i];
+        }
+    }
+    __syncthreads();
+    finish_from_list(sm, nlist, topk, n, out);
+}
+
 }  // namespace
+
+// [list sizes (n_rows ints, padded to 16 bytes) | keys (n_rows x kCap) | positions (n_rows x kCap)]
+static size_t list_sizes_bytes(int n_rows) { return ((size_t)n_rows * sizeof(int) + 15) & ~(size_t)15; }
+
+size_t topk_list_ws_bytes(int n_rows) {
+    return n_rows <= 0 ? 0
+                       : list_sizes_bytes(n_rows) + (size_t)n_rows * kCap * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
+hipError_t launch_topk_list(const float* scores, int64_t stride, const uint32_t* hist, int32_t* idx, int topk,
+                            const RowMap& map, int n_rows, int max_len, void* ws, hipStream_t st) {
+    if (n_rows <= 0) return hipSuccess;
+    int* lcount = (int*)ws;
+    uint32_t* lkey = (uint32_t*)((uint8_t*)ws + list_sizes_bytes(n_rows));
+    int32_t* lpos = (int32_t*)(lkey + (size_t)n_rows * kCap);
+    hipLaunchKernelGGL(topk_list_append_kernel, dim3((max_len + kSeg - 1) / kSeg, n_rows), dim3(kThreads), 0, st,
+                       scores, stride, hist, topk, map, n_rows, lkey, lpos, lcount);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_list_finish_kernel, dim3(n_rows), dim3(kThreads), 0, st, scores, stride, hist, idx,
+                       topk, map, n_rows, lkey, lpos);
+    return hipGetLastError();
+}
 
 int topk_segments(int max_len) { return (max_len + kSeg - 1) / kSeg; }
 
