@@ -161,3 +161,24 @@ def test_decode_forward_topk_equals_two_stage(cuda):
     assert not bad, f"decode rows differ: {bad}"
     a2 = fused_idx(dims, inp, cuda)
     assert torch.equal(a, a2)
+
+
+def test_decode_forward_topk_many_rows(cuda):
+    # 160 decode rows (more than the segmented dsa_topk handles) of mixed lengths, some below k,
+    # some at segment boundaries; every fifth row has only five distinct keys (a crowded
+    # threshold bin)
+    dims = dsa_inputs.PROD
+    rng = np.random.default_rng(12)
+    lens = [int(x) for x in rng.integers(1, 40000, 160)]
+    lens[:4] = [2048, 2049, 16384, 32769]
+    say(f"decode forward index rows vs indexer_scores + topk, {len(lens)} rows")
+    inp = dsa_inputs.decode_inputs(dims=dims, seed=13, device=cuda, lens=lens, needles=False)
+    for b in range(4, len(lens), 5):
+        k0 = inp["cu_k"][b]
+        sel = torch.arange(lens[b], device=cuda) % 5 + k0
+        inp["k8"][k0:k0 + lens[b]] = inp["k8"][sel]
+        inp["k_scale"][k0:k0 + lens[b]] = inp["k_scale"][sel]
+    a = fused_idx(dims, inp, cuda)
+    b_ = decode_unfused_idx(dims, inp, cuda)
+    bad = torch.nonzero((a != b_).any(dim=1)).flatten().tolist()
+    assert not bad, f"decode rows differ: {bad[:10]}"
