@@ -90,7 +90,7 @@ struct MqaCfg {
     static constexpr int VBYTES = DV * 2;                  // bytes of its value part
     static constexpr int MAXK = (INSTRS + NDW - 1) / NDW;  // direct loads per loading wave and block
     static constexpr int LOADS_PER_WAVE = INSTRS / NDW;    // fewest of a loading wave per block
-    static constexpr int QK_AHEAD = KH < 6 ? KH : 6;       // logit operand reads kept in flight
+    static constexpr int QK_AHEAD = KH < 9 ? KH : 9;       // logit operand reads kept in flight
     // Per-lane LDS offsets are kept for TLQ logit slices and TLV value tiles only: the rest
     // differ by a multiple of the swizzle period and reach the reads as immediate offsets.
     static constexpr int W = RV::SWZ_BITS;
