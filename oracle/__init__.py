@@ -57,6 +57,11 @@ def lib():
         L.orc_topk_rows_f32.argtypes = [I, P, P, I64, I, P]
         L.orc_sparse_mqa.argtypes = [I, I, I, D, I, P, P, I, P, P, P]
         L.orc_dense_causal.argtypes = [I, I, I, D, I, P, P, P, P, P]
+        L.orc_encode_e4m3_n.argtypes = [I64, P, P]
+        L.orc_rope_f32.argtypes = [I, I, P, I64, P, P, I64, I, P]
+        L.orc_quantize_rows_e4m3.argtypes = [I, I, P, P, P]
+        L.orc_cache_append.argtypes = [I, I, I, P, P, P, P, P, I64, I, P, P, P, P]
+        L.orc_indexer_kl.argtypes = [I, I, D, I, P, P, P, I, P, P, I64, P, P]
         L.orc_num_threads.restype = I
         _lib = L
     return _lib
@@ -169,6 +174,7 @@ def sparse_mqa(q_bits, kv_bits, idx, v_dim: int, sm_scale: float):
     kv, pkv = _c(kv_bits, np.uint16)
     ix, pix = _c(idx, np.int32)
     k = ix.shape[1] if ix.ndim == 2 else 0
+    assert ix.shape[0] == T and (ix.size == 0 or int(ix.max()) < kv.shape[0]), "one index row per query row"
     out = np.zeros((T, H, v_dim), np.float64)
     lse = np.zeros((T, H), np.float64)
     if T == 0:
@@ -184,6 +190,7 @@ def dense_causal(q_bits, kv_bits, pos, v_dim: int, sm_scale: float):
     T, H, Dqk = q.shape
     kv, pkv = _c(kv_bits, np.uint16)
     p, pp = _c(pos, np.int32)
+    assert p.shape == (T,) and (T == 0 or int(p.max()) < kv.shape[0]), "one position per query row, within kv"
     out = np.zeros((T, H, v_dim), np.float64)
     lse = np.zeros((T, H), np.float64)
     lib().orc_dense_causal(H, Dqk, v_dim, float(sm_scale), T, pp, pq, pkv,
@@ -218,48 +225,24 @@ def forward_rows(inp: dict, rows, seq: int = 0):
 # ---- cache producer: RoPE, FP8 quantisation, cache append ---------------------------------
 # (DeepSeek-V3.2-Exp lightning-indexer walk-through, step 2: rotary position encoding of the
 # first 64 dims of the indexer query and key, then FP8 quantisation of both with the key
-# codes and their scale kept in the cache.)  The rotation and the quantiser are evaluated in
-# float32 with every product, sum and quotient rounded separately, the precision in which the
-# GPU path decides each FP8 code, so both sides make the same rounding decisions.
-
-_E4M3_VALUES = None
-
-
-def _e4m3_table():
-    """(finite values ascending, their codes) of the e4m3fn format: 1 sign, 4 exponent
-    (bias 7), 3 mantissa bits; exponent 0 is subnormal (m * 2^-9); code 0x7f/0xff are NaN."""
-    global _E4M3_VALUES
-    if _E4M3_VALUES is None:
-        codes = [c for c in range(256) if (c & 0x7f) != 0x7f and c != 0x80]  # -0 folded into +0
-        vals = decode_e4m3(np.array(codes, np.uint8))
-        order = np.argsort(vals, kind="stable")
-        _E4M3_VALUES = (vals[order], np.array(codes, np.uint8)[order])
-    return _E4M3_VALUES
-
+# codes and their scale kept in the cache.)  oracle.c evaluates the rotation and the
+# quantiser in float32 with every product, sum and quotient rounded separately, the precision
+# in which the GPU path decides each FP8 code, so both sides make the same rounding decisions.
 
 def encode_e4m3(x) -> np.ndarray:
-    """Round each value to the nearest e4m3fn value, ties to the even code (mantissa bit 0
-    clear), saturating at +-448 (the format has no infinity).  -0 and values that round to
-    zero from below give code 0x80; NaN gives 0x7f.  Brute force over the 254 finite values."""
-    vals, codes = _e4m3_table()
-    x = np.asarray(x, np.float64)
-    flat = x.reshape(-1)
-    out = np.empty(flat.shape, np.uint8)
-    for i, v in enumerate(flat):
-        if np.isnan(v):
-            out[i] = 0x7F
-            continue
-        a = min(abs(v), 448.0)
-        d = np.abs(vals - a)
-        best = np.flatnonzero(d == d.min())
-        c = codes[best[0]]
-        if len(best) > 1:  # a tie between two neighbours: the even mantissa wins
-            even = [b for b in best if (codes[b] & 1) == 0]
-            c = codes[even[0]]
-        if np.signbit(v):
-            c = c | 0x80
-        out[i] = c
-    return out.reshape(x.shape)
+    """Nearest e4m3fn code of each float32 value, ties to the even code, saturating at +-448;
+    the sign bit follows the input (-0 -> 0x80), NaN -> 0x7f."""
+    a, p = _c(x, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib().orc_encode_e4m3_n(a.size, p, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def _tables(cos_tab, sin_tab):
+    c, pc = _c(cos_tab, np.float32)
+    s, ps = _c(sin_tab, np.float32)
+    assert c.shape == s.shape and c.ndim == 2
+    return c, pc, s, ps, c.shape[1]
 
 
 def rope_f32(x, pos, cos_tab, sin_tab, rope_dim: int):
@@ -267,37 +250,46 @@ def rope_f32(x, pos, cos_tab, sin_tab, rope_dim: int):
     pairs (2i, 2i+1) rotate by the table's angle for (pos, i),
         r0 = x0*c - x1*s,  r1 = x0*s + x1*c,
     each product and sum rounded to float32; the other dims pass unchanged."""
-    x = np.array(x, np.float32, copy=True)
-    c = np.float32(cos_tab[pos, : rope_dim // 2])
-    s = np.float32(sin_tab[pos, : rope_dim // 2])
-    x0 = x[..., 0:rope_dim:2].copy()
-    x1 = x[..., 1:rope_dim:2].copy()
-    r0 = np.float32(np.float32(x0 * c) - np.float32(x1 * s))
-    r1 = np.float32(np.float32(x0 * s) + np.float32(x1 * c))
-    x[..., 0:rope_dim:2] = r0
-    x[..., 1:rope_dim:2] = r1
-    return x
+    a, pa = _c(x, np.float32)
+    c, pc, s, ps, stride = _tables(cos_tab, sin_tab)
+    assert rope_dim // 2 <= stride and 0 <= int(pos) < c.shape[0]
+    d = a.shape[-1]
+    out = np.empty(a.shape, np.float32)
+    lib().orc_rope_f32(a.size // d, d, pa, int(pos), pc, ps, stride, rope_dim,
+                       out.ctypes.data_as(ctypes.c_void_p))
+    return out
 
 
 def quantize_row_e4m3(x):
     """One scale per row of x[..., d] (float32): amax/448 (1 for an all-zero row), codes of
     x / scale clamped to +-448, all in float32."""
-    x = np.asarray(x, np.float32)
-    amax = np.max(np.abs(x), axis=-1)
-    scale = np.where(amax > 0, np.float32(amax / np.float32(448.0)), np.float32(1.0)).astype(np.float32)
-    y = np.clip(np.float32(x / scale[..., None]), np.float32(-448.0), np.float32(448.0))
-    return encode_e4m3(y), scale
+    a, pa = _c(x, np.float32)
+    d = a.shape[-1]
+    codes = np.empty(a.shape, np.uint8)
+    scale = np.empty(a.shape[:-1], np.float32)
+    lib().orc_quantize_rows_e4m3(a.size // d, d, pa, codes.ctypes.data_as(ctypes.c_void_p),
+                                 scale.ctypes.data_as(ctypes.c_void_p))
+    return codes, scale
 
 
 def cache_append(q_idx, k_idx, pos, cos_tab, sin_tab, rope_dim: int):
     """New tokens' indexer entries: q_idx [n, H, d] and k_idx [n, d] float32 at positions
     pos[n] -> (q8 [n, H, d], q_scale [n, H], k8 [n, d], k_scale [n])."""
-    q8, qs, k8, ks = [], [], [], []
-    for i, p in enumerate(pos):
-        a, sa = quantize_row_e4m3(rope_f32(q_idx[i], p, cos_tab, sin_tab, rope_dim))
-        b, sb = quantize_row_e4m3(rope_f32(k_idx[i], p, cos_tab, sin_tab, rope_dim))
-        q8.append(a); qs.append(sa); k8.append(b); ks.append(sb)
-    return np.stack(q8), np.stack(qs), np.stack(k8), np.array(ks, np.float32)
+    q, pq = _c(q_idx, np.float32)
+    k, pk = _c(k_idx, np.float32)
+    ps_, ppos = _c(pos, np.int64)
+    n, H, d = q.shape
+    assert k.shape == (n, d) and ps_.shape == (n,)
+    c, pc, s, pss, stride = _tables(cos_tab, sin_tab)
+    assert rope_dim // 2 <= stride and (n == 0 or (ps_.min() >= 0 and ps_.max() < c.shape[0]))
+    q8 = np.empty((n, H, d), np.uint8)
+    qs = np.empty((n, H), np.float32)
+    k8 = np.empty((n, d), np.uint8)
+    ks = np.empty(n, np.float32)
+    if n:
+        vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        lib().orc_cache_append(n, H, d, pq, pk, ppos, pc, pss, stride, rope_dim, vp(q8), vp(qs), vp(k8), vp(ks))
+    return q8, qs, k8, ks
 
 
 def indexer_kl(q_bits, kv_bits, lse, slots, scores, sm_scale: float):
@@ -311,26 +303,23 @@ def indexer_kl(q_bits, kv_bits, lse, slots, scores, sm_scale: float):
       q_bits [T, H, Dqk] uint16 (bf16), kv_bits [S, Dqk] uint16 (the rows of the row's
       sequence), lse [T, H] float (natural log), slots: T arrays of positions (-1 = empty),
       scores: T arrays with I[t, s] at index s."""
-    q = decode_bf16(q_bits)
-    kv = decode_bf16(kv_bits)
-    lse = np.asarray(lse, np.float64)
-    T = q.shape[0]
+    q, pq = _c(q_bits, np.uint16)
+    T, H, Dqk = q.shape
+    kv, pkv = _c(kv_bits, np.uint16)
+    ls, pls = _c(lse, np.float64)
+    k = max([len(s) for s in slots] + [1])
+    sl = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        sl[t, : len(slots[t])] = slots[t]
+    width = max([len(s) for s in scores] + [1])
+    sc = np.zeros((T, width), np.float64)
+    for t in range(T):
+        sc[t, : len(scores[t])] = scores[t]
+    assert sl.max() < min(kv.shape[0], width), "slot outside the key rows or the score row"
     kl = np.zeros(T)
     rev = np.zeros(T)
-    for t in range(T):
-        pos = np.asarray(slots[t], np.int64)
-        pos = pos[pos >= 0]
-        if len(pos) == 0:
-            continue
-        z = sm_scale * (kv[pos] @ q[t].T)                  # [slots, H]
-        P = np.exp(z - lse[t][None, :]).sum(axis=1)
-        P = P / P.sum()
-        I = np.asarray(scores[t], np.float64)[pos]
-        m = I.max()
-        logQ = I - (m + np.log(np.exp(I - m).sum()))
-        Q = np.exp(logQ)
-        with np.errstate(divide="ignore", invalid="ignore"):
-            logP = np.log(P)
-            kl[t] = np.sum(np.where(P > 0, P * (logP - logQ), 0.0))
-            rev[t] = np.sum(Q * (logQ - logP))
+    if T:
+        lib().orc_indexer_kl(H, Dqk, float(sm_scale), T, pq, pkv, pls, k, sl.ctypes.data_as(ctypes.c_void_p),
+                             sc.ctypes.data_as(ctypes.c_void_p), width, kl.ctypes.data_as(ctypes.c_void_p),
+                             rev.ctypes.data_as(ctypes.c_void_p))
     return kl, rev

@@ -20,6 +20,11 @@
  *    dot product, ReLU, weighted head sum; top-k positions).
  *  - "DeepSeek-V3.2 explained", sections 二.1-二.4 (DSA = attention over the top-k index
  *    set; 576-wide latent row = 512 latent + 64 rope; selected entries shared by all heads).
+ *  - Lightning-indexer walk-through, step 2 (rotary encoding of the indexer query and key,
+ *    FP8 quantisation of both, key codes and scale cached): the cache producer, in float32.
+ *  - "DeepSeek-V3.2-Exp" overview, "训练"; "DeepSeek-V3.2-Exp解析" section 二; deep dive
+ *    section 3 (indexer trained towards the head-summed, L1-normalised main attention with a
+ *    KL divergence): the indexer training target, forward only.
  */
 #include <math.h>
 #include <stdint.h>
@@ -330,6 +335,170 @@ void orc_dense_causal(int H, int Dqk, int Dv, double sm, int T, const int32_t* p
             }
         }
         free(p);
+    }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Cache producer: RoPE, FP8 encoding, per-row quantiser                                */
+/* ------------------------------------------------------------------------------------ */
+
+/* Lightning-indexer walk-through, step 2: the indexer query and key get a rotary encoding
+ * of their first dims, are quantised to FP8 and the key codes are cached with their scale.
+ * Everything here runs in float32 with each product, sum and quotient rounded on its own
+ * (this file is built with -ffp-contract=off), the precision in which the GPU path decides
+ * each FP8 code, so that both sides take the same rounding decisions. */
+
+/* Nearest e4m3fn code of x: a search over the 127 non-negative finite codes for the value
+ * closest to |x| (|x| above 448 saturates to 448: the format has no infinity); of two equally
+ * close neighbours the one with an even code (mantissa bit 0 clear) wins.  The sign bit is
+ * copied from x, so -0 and negative values that round to zero give 0x80.  NaN gives 0x7f. */
+uint8_t orc_encode_e4m3(float x) {
+    if (isnan(x)) return 0x7F;
+    double a = fabs((double)x);
+    if (a > 448.0) a = 448.0;
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(orc_e4m3((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(signbit(x) ? (best | 0x80) : best);
+}
+
+void orc_encode_e4m3_n(int64_t n, const float* x, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_encode_e4m3(x[i]);
+}
+
+/* Rotary encoding of rows x[r, 0..d-1] (float32) at position pos: the pairs (2i, 2i+1) with
+ * 2i < rope_dim rotate by the angle whose cosine and sine are cos_tab / sin_tab[pos *
+ * tab_stride + i]:
+ *     r0 = x0*c - x1*s,   r1 = x0*s + x1*c     (each product and difference rounded to fp32);
+ * the dims from rope_dim on are copied unchanged. */
+void orc_rope_f32(int n_rows, int d, const float* x, int64_t pos, const float* cos_tab,
+                  const float* sin_tab, int64_t tab_stride, int rope_dim, float* out) {
+    const float* c = cos_tab + pos * tab_stride;
+    const float* s = sin_tab + pos * tab_stride;
+    for (int r = 0; r < n_rows; ++r) {
+        const float* xr = x + (int64_t)r * d;
+        float* o = out + (int64_t)r * d;
+        for (int i = 0; i < d; ++i) o[i] = xr[i];
+        for (int i = 0; 2 * i + 1 < rope_dim; ++i) {
+            float x0 = xr[2 * i], x1 = xr[2 * i + 1];
+            float a = x0 * c[i], b = x1 * s[i];
+            float e = x0 * s[i], f = x1 * c[i];
+            o[2 * i] = a - b;
+            o[2 * i + 1] = e + f;
+        }
+    }
+}
+
+/* One scale per row of x[r, 0..d-1] (float32): amax/448 (1 for an all-zero row), then the
+ * codes of x / scale, clamped to +-448. */
+void orc_quantize_rows_e4m3(int n_rows, int d, const float* x, uint8_t* codes, float* scale) {
+    for (int r = 0; r < n_rows; ++r) {
+        const float* xr = x + (int64_t)r * d;
+        float amax = 0.0f;
+        for (int i = 0; i < d; ++i) {
+            float a = fabsf(xr[i]);
+            if (a > amax) amax = a;
+        }
+        float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scale[r] = sc;
+        for (int i = 0; i < d; ++i) {
+            float y = xr[i] / sc;
+            if (y > 448.0f) y = 448.0f;
+            if (y < -448.0f) y = -448.0f;
+            codes[(int64_t)r * d + i] = orc_encode_e4m3(y);
+        }
+    }
+}
+
+/* The cache producer for n new tokens at positions pos[i]: RoPE on the indexer query
+ * q_idx[i] ([H][d]) and key k_idx[i] ([d]) over the first rope_dim dims, then one scale and
+ * code row per query head and for the key.  Outputs q8 [n][H][d], q_scale [n][H],
+ * k8 [n][d], k_scale [n]. */
+void orc_cache_append(int n, int H, int d, const float* q_idx, const float* k_idx, const int64_t* pos,
+                      const float* cos_tab, const float* sin_tab, int64_t tab_stride, int rope_dim,
+                      uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale) {
+#pragma omp parallel
+    {
+        float* rot = (float*)malloc(sizeof(float) * (size_t)H * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < n; ++i) {
+            orc_rope_f32(H, d, q_idx + (int64_t)i * H * d, pos[i], cos_tab, sin_tab, tab_stride, rope_dim, rot);
+            orc_quantize_rows_e4m3(H, d, rot, q8 + (int64_t)i * H * d, q_scale + (int64_t)i * H);
+            orc_rope_f32(1, d, k_idx + (int64_t)i * d, pos[i], cos_tab, sin_tab, tab_stride, rope_dim, rot);
+            orc_quantize_rows_e4m3(1, d, rot, k8 + (int64_t)i * d, k_scale + i);
+        }
+        free(rot);
+    }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Indexer training target (forward only)                                               */
+/* ------------------------------------------------------------------------------------ */
+
+/* DeepSeek-V3.2-Exp overview, "训练"; 解析 section 二; deep dive section 3: the indexer is
+ * trained towards the main attention summed over heads and L1-normalised along the keys,
+ * with a KL divergence; in the sparse stage both sides are restricted to the selected set.
+ * For query row t over its slots (entries of slots[t*k ..] that are not -1):
+ *     P[s] = sum_h exp(sm * q[t,h,:] . kv[s,:] - lse[t,h]),   P /= sum_s P[s]
+ *     Q    = softmax over the slots of the indexer scores I[t,s] = scores[t*score_stride + s]
+ *     kl[t] = sum_{P>0} P (ln P - ln Q),   rev[t] = sum Q (ln Q - ln P)  (+inf if some P = 0)
+ * A row without slots gets 0 and 0.  q: [T][H][Dqk] bf16 bits, kv: rows of the sequence. */
+void orc_indexer_kl(int H, int Dqk, double sm, int T, const uint16_t* q, const uint16_t* kv,
+                    const double* lse, int k, const int32_t* slots, const double* scores,
+                    int64_t score_stride, double* kl, double* rev) {
+#pragma omp parallel
+    {
+        double* P = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+        double* lq = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+        double* qd = (double*)malloc(sizeof(double) * (size_t)H * (size_t)Dqk);
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < T; ++t) {
+            const int32_t* sel = slots + (int64_t)t * k;
+            const double* I = scores + (int64_t)t * score_stride;
+            kl[t] = 0.0;
+            rev[t] = 0.0;
+            for (int x = 0; x < H * Dqk; ++x) qd[x] = orc_bf16(q[(int64_t)t * H * Dqk + x]);
+            int n = 0;
+            double psum = 0.0, imax = -INFINITY;
+            for (int i = 0; i < k; ++i) {
+                if (sel[i] < 0) continue;
+                const uint16_t* crow = kv + (int64_t)sel[i] * Dqk;
+                double p = 0.0;
+                for (int h = 0; h < H; ++h) {
+                    double z = 0.0;
+                    for (int dd = 0; dd < Dqk; ++dd) z += qd[(int64_t)h * Dqk + dd] * orc_bf16(crow[dd]);
+                    p += exp(sm * z - lse[(int64_t)t * H + h]);
+                }
+                P[n] = p;
+                lq[n] = I[sel[i]];
+                psum += p;
+                if (lq[n] > imax) imax = lq[n];
+                ++n;
+            }
+            if (n == 0) continue;
+            double esum = 0.0;
+            for (int i = 0; i < n; ++i) esum += exp(lq[i] - imax);
+            const double lse_i = imax + log(esum);
+            double a = 0.0, b = 0.0;
+            for (int i = 0; i < n; ++i) {
+                const double p = P[i] / psum;
+                const double lQ = lq[i] - lse_i;
+                const double lP = log(p);  /* -inf for p = 0 */
+                if (p > 0.0) a += p * (lP - lQ);
+                b += exp(lQ) * (lQ - lP);
+            }
+            kl[t] = a;
+            rev[t] = b;
+        }
+        free(qd);
+        free(lq);
+        free(P);
     }
 }
 
