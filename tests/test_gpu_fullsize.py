@@ -1,9 +1,14 @@
 """GPU parity at the full prefill sizes (65,536 and 131,072 tokens), in the launch configuration
-bench.py times (one dsa_forward with the default workspace: 8192-row passes), on sampled rows
-the oracle computes one by one: the selected sets (identical except positions within 1e-3 of
-the oracle's k-th score), the attention output and lse on the GPU's own index rows (max abs
-2e-2, relative L2 1e-2, lse 2e-3), and needle recall equal to the oracle's.  Only the sampled
-query rows and the key side are copied to the host."""
+bench.py times (one dsa_forward with the default workspace: 8192-row passes), on the rows the
+oracle computes one by one:
+  - 8 blocks of 64 consecutive query rows at seeded offsets, the last row, and 32 seeded rows
+    below 2048 (where the top-k keeps every earlier position);
+  - the query row of every planted needle at 65,536 (1,024 needles) and of 512 seeded needles
+    at 131,072.
+Checked: the selected sets (identical except positions within 1e-3 of the oracle's k-th
+score), the attention output and lse on the GPU's own index rows (max abs 2e-2, relative L2
+1e-2, lse 2e-3), and needle recall equal to the oracle's.  Only the sampled query rows and the
+key side are copied to the host."""
 import numpy as np
 import pytest
 import torch
@@ -20,41 +25,82 @@ def say(msg):
     print(f"[gpu-test] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("L", [65536, 131072])
-def test_forward_full_size_sampled_rows(cuda, L):
+_cache = {}
+
+
+def forward_full(L, dev):
+    """One dsa_forward over the whole L-token prefill (kept for the tests of the same L)."""
+    if _cache.get("L") == L:
+        return _cache["res"]
+    _cache.clear()
+    torch.cuda.empty_cache()
     dims = dsa_inputs.PROD
-    say(f"forward prod L={L} (8192-row passes), sampled rows against the oracle")
-    inp = dsa_inputs.prefill_inputs(L, dims, seed=0, device=cuda)
-    batch = dsa.Batch(inp["cu_q"], inp["cu_k"], device=cuda)
-    out = torch.empty(L, dims.n_heads, dims.v_dim, dtype=torch.bfloat16, device=cuda)
-    lse = torch.empty(L, dims.n_heads, dtype=torch.float32, device=cuda)
-    idx = torch.empty(L, dims.topk, dtype=torch.int32, device=cuda)
-    ws = torch.empty(dsa.workspace_size(dims, batch), dtype=torch.uint8, device=cuda)
+    inp = dsa_inputs.prefill_inputs(L, dims, seed=0, device=dev)
+    batch = dsa.Batch(inp["cu_q"], inp["cu_k"], device=dev)
+    out = torch.empty(L, dims.n_heads, dims.v_dim, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(L, dims.n_heads, dtype=torch.float32, device=dev)
+    idx = torch.empty(L, dims.topk, dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.workspace_size(dims, batch), dtype=torch.uint8, device=dev)
     dsa.forward(dims, batch, inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"], inp["q"], inp["kv"],
                 out, lse, idx, ws)
     torch.cuda.synchronize()
     del ws
-    rng = np.random.default_rng(L)
-    needles = inp["needles"]
-    nrows = sorted(set(t for t, s in needles[::211]))[:4]
-    rows = sorted(set([0, 1, 2047, 2048, 2049, 8191, 8192, L // 2, L - 1] + [int(x) for x in rng.integers(2048, L, 3)]
-                      + nrows))
-    r = torch.tensor(rows, device=cuda)
-    q8, qs, w = host(inp["q8"][r]), host(inp["q_scale"][r]), host(inp["w"][r])
-    q = host(inp["q"][r])
-    k8, ks, kv = host(inp["k8"]), host(inp["k_scale"]), host(inp["kv"])
+    keys = dict(k8=host(inp["k8"]), k_scale=host(inp["k_scale"]), kv=host(inp["kv"]))
+    res = (dims, inp, out, lse, idx, keys)
+    _cache.update(L=L, res=res)
+    return res
+
+
+def block_rows(L, seed):
+    rng = np.random.default_rng(seed)
+    starts = rng.choice((L - 64) // 64, 8, replace=False) * 64 + rng.integers(0, 64, 8)
+    rows = set()
+    for s in starts:
+        rows.update(range(int(s), int(s) + 64))
+    rows.add(L - 1)
+    rows.update(int(x) for x in rng.choice(2048, 32, replace=False))
+    return sorted(rows)
+
+
+def check_rows(L, rows, dev, what):
+    dims, inp, out, lse, idx, keys = forward_full(L, dev)
+    r = torch.tensor(rows, device=dev)
+    q8, qs, w, q = host(inp["q8"][r]), host(inp["q_scale"][r]), host(inp["w"][r]), host(inp["q"][r])
     pos = np.asarray(rows, np.int64)
-    scores = oracle.indexer_rows(q8, qs, w, k8, ks, np.arange(len(rows)), pos)
+    scores = oracle.indexer_rows(q8, qs, w, keys["k8"], keys["k_scale"], np.arange(len(rows)), pos)
     ref_idx = oracle.topk_rows(scores, dims.topk)
     gi = host(idx[r])
     ndiff = sum(check_sets(gi[i], ref_idx[i], scores[i], dims.topk) for i in range(len(rows)))
-    ro, rl = oracle.sparse_mqa(q, kv, gi, dims.v_dim, dims.sm_scale)
-    check_attention(host(out[r]), ro, what=f"L={L} forward")
+    ro, rl = oracle.sparse_mqa(q, keys["kv"], gi, dims.v_dim, dims.sm_scale)
+    check_attention(host(out[r]), ro, what=f"L={L} {what}")
     np.testing.assert_allclose(host(lse[r]), rl, rtol=0, atol=2e-3)
-    planted = [(t, s) for t, s in needles if t in set(rows)]
     row_of = {t: i for i, t in enumerate(rows)}
-    rec_g = np.mean([s in set(gi[row_of[t]]) for t, s in planted]) if planted else 1.0
-    rec_o = np.mean([s in set(ref_idx[row_of[t]]) for t, s in planted]) if planted else 1.0
-    say(f"L={L}: {len(rows)} rows, set differences {ndiff}, needle recall gpu {rec_g:.3f} oracle {rec_o:.3f} "
-        f"over {len(planted)}")
+    planted = [(t, s) for t, s in inp["needles"] if t in row_of]
+    rec_g = float(np.mean([s in set(gi[row_of[t]]) for t, s in planted])) if planted else 1.0
+    rec_o = float(np.mean([s in set(ref_idx[row_of[t]]) for t, s in planted])) if planted else 1.0
+    say(f"L={L} {what}: {len(rows)} rows, set differences {ndiff}, needle recall gpu {rec_g:.4f} "
+        f"oracle {rec_o:.4f} over {len(planted)} needles")
     assert rec_g == rec_o
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _release():
+    yield
+    _cache.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("L,kind", [(65536, "blocks"), (65536, "needles"), (131072, "blocks"), (131072, "needles")])
+def test_forward_full_size_sampled_rows(cuda, L, kind):
+    if kind == "blocks":
+        say(f"forward prod L={L}: 8 seeded 64-row blocks, the last row, 32 rows below 2048")
+        check_rows(L, block_rows(L, seed=L), cuda, "row blocks")
+        return
+    n_needles = None if L <= 65536 else 512
+    say(f"forward prod L={L}: query rows of {'every' if n_needles is None else n_needles} planted needles")
+    dims, inp, *_ = forward_full(L, cuda)
+    needles = inp["needles"]
+    if n_needles is not None:
+        pick = np.random.default_rng(L + 1).choice(len(needles), n_needles, replace=False)
+        needles = [needles[i] for i in sorted(pick)]
+    check_rows(L, sorted(set(t for t, s in needles)), cuda, "needle rows")

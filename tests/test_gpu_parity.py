@@ -1,6 +1,8 @@
 """GPU parity of every stage and of the whole path against the CPU oracle, through the C ABI.
 
-Tolerances: indexer |g - o| <= 1e-3 * M (M = the score with |w| in place of w); top-k on the
+Tolerances: indexer |g - o| <= 1e-3 * M + eps_acc * A (M = the score with |w| in place of w,
+A = the same with sign-free codes, eps_acc = twice the FP8 MFMA accumulation error that
+tests/test_gpu_fp8_accumulation.py measures and asserts); top-k on the
 same fp32 arrays bit-exact; end-to-end sets identical except positions within 1e-3 of the
 oracle's k-th score; attention max abs 2e-2 and relative L2 1e-2 against the oracle run on
 the GPU's own index rows."""
@@ -395,14 +397,25 @@ def test_forward_decode_small(cuda):
         compare_forward_rows(inp, h, out, lse, idx, [0], dims, f"decode seq {b}", seq=b)
 
 
-def test_forward_decode_32_full_size_sampled(cuda):
-    say("forward decode B=32 lens U[32768,131072], sampled sequences")
+def test_forward_decode_32_full_size_all_sequences(cuda):
+    say("forward decode B=32 lens U[32768,131072], every sequence + needle recall")
+    from concurrent.futures import ThreadPoolExecutor
+
     dims = dsa_inputs.PROD
     inp = dsa_inputs.decode_inputs(32, dims=dims, seed=0, device=cuda)
     out, lse, idx = run_forward(inp, dims, cuda)
     h = host_inputs(inp)
-    for b in (0, 13, 31):
-        compare_forward_rows(inp, h, out, lse, idx, [0], dims, f"decode32 seq {b}", seq=b)
+    # one oracle row per sequence: the sequences run side by side (the oracle call releases
+    # the interpreter while it computes)
+    with ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(lambda b: compare_forward_rows(inp, h, out, lse, idx, [0], dims, f"decode32 seq {b}",
+                                                         seq=b), range(32)))
+    gi = idx.cpu().numpy()
+    rec_g = np.mean([s in set(gi[b]) for b, s in inp["needles"]])
+    rec_o = np.mean([s in set(res[b][0]["idx"][0]) for b, s in inp["needles"]])
+    say(f"decode32: set differences {sum(r[1] for r in res)}, needle recall gpu {rec_g:.4f} oracle {rec_o:.4f} "
+        f"over {len(inp['needles'])} needles")
+    assert rec_g == rec_o
 
 
 def test_forward_ragged_prefill_batch(cuda):
