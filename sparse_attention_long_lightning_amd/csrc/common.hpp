@@ -22,7 +22,8 @@ constexpr int kMaxTopk = 8192;  // largest k accepted (k = 2048 in the DeepSeek-
 //      query row row0 + i of the packed query arrays;
 //  batch mode: row i is a global query row; its sequence b is found in cu_q.
 //  paged caches (pages != nullptr): position p of sequence s is cache row
-//      pages[s * pages_per_seq + p / kPage] * kPage + p % kPage.
+//      pages[s * pages_per_seq + p / kPage] * kPage + p % kPage
+//  of a pool of pool_rows rows (0: not given, page ids are then trusted).
 struct RowMap {
     const int32_t* cu_q;
     const int32_t* cu_k;
@@ -32,6 +33,7 @@ struct RowMap {
     int kbase;
     const int32_t* pages = nullptr;
     int pages_per_seq = 0;
+    int64_t pool_rows = 0;
 };
 
 constexpr int kPage = 64;  // positions per cache page
@@ -41,6 +43,8 @@ struct RowInfo {
     int pos;    // absolute position p (keys 0..p)
     int kbase;  // packed key row of position 0
     int seq;    // sequence of the row
+    int lim;    // largest position an index slot may name: len_k - 1 of the row's sequence in
+                // batch mode, p in single-sequence mode (whose index rows the top-k wrote)
 };
 
 // Cache row of position p of the row's sequence.
@@ -56,6 +60,7 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& m, int i) {
         r.pos = m.pos0 + i;
         r.kbase = m.kbase;
         r.seq = 0;
+        r.lim = r.pos;
         return r;
     }
     int lo = 0, hi = m.n_seqs - 1;  // last b with cu_q[b] <= i
@@ -70,7 +75,19 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& m, int i) {
     r.pos = lk - lq + (i - m.cu_q[b]);
     r.kbase = m.cu_k[b];
     r.seq = b;
+    r.lim = lk - 1;
     return r;
+}
+
+// Cache row that index slot value id names for the row, or -1 when the slot is empty or its
+// value cannot be loaded: -1 and every value outside [0, lim], and with paged caches of known
+// pool size a page id outside the pool.  Gathers load only rows this returns, so an index row
+// with out-of-range entries can never make them read outside the caches.
+__device__ __forceinline__ int64_t slot_row(const RowMap& m, const RowInfo& r, int id) {
+    if ((unsigned)id > (unsigned)r.lim) return -1;
+    const int64_t row = cache_row(m, r, id);
+    if (m.pages != nullptr && m.pool_rows > 0 && (row < 0 || row >= m.pool_rows)) return -1;
+    return row;
 }
 
 // Order-preserving map of a float score to an unsigned key: larger score -> larger key,
@@ -148,6 +165,17 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
         "global_load_lds_dwordx4 %1, %2"
         :
         : "s"(lds_base), "v"(off), "s"(base)
+        : "memory", "m0");
+}
+// The same from a full 64-bit address per lane (no scalar base): for rows beyond 4 GiB of
+// the base, e.g. in a large page pool.
+__device__ __forceinline__ void dma16_at(const void* addr, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds_base), "v"(addr)
         : "memory", "m0");
 }
 // The same with 4 bytes per lane: lane i's dword lands at lds_base + 4 * i.

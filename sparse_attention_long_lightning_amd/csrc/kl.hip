@@ -133,10 +133,14 @@ __global__ __launch_bounds__(kKlThreads, 2) void indexer_kl_kernel(
     const bool paged = map.pages != nullptr;
     const uint8_t* kvb = (const uint8_t*)(paged ? kv : kv + (int64_t)ri.kbase * DQK);
 
+    // a slot's position, or -1 when it is empty or names no loadable row (values outside the
+    // sequence, page ids outside a pool of known size): such slots take no part, so no load or
+    // score read ever leaves the caches
     auto slot_id = [&](int b, int s) {
         const int j = b * kKlSlots + s;
         if (j >= jn) return -1;
-        return dense ? j : irow[j];
+        const int id = dense ? j : irow[j];
+        return slot_row(map, ri, id) >= 0 ? id : -1;
     };
     auto kv_row = [&](int id) -> int64_t { return paged ? cache_row(map, ri, id) : (int64_t)id; };
 
@@ -163,11 +167,22 @@ __global__ __launch_bounds__(kKlThreads, 2) void indexer_kl_kernel(
 
     // gather of block b: load instruction i (k-slice i) moves chunk 2i + l / 32 of slot l % 32
     // to buf + i * 1024 + 16 l; wave w issues instructions w, w + 4, ...  An empty slot loads
-    // row 0 (its column of the product is never used).  A row's byte offset must fit in 32 bits.
+    // row 0 (its column of the product is never used).  Packed caches load at 32-bit offsets
+    // from the sequence's first row (a sequence is shorter than 2^32 / 1152 positions, checked
+    // on the host); paged caches at 64-bit addresses, so a page pool may exceed 4 GiB.
     auto load_block = [&](int b) {
         const int id = ids[b & 1][lane & 31];
-        const uint32_t roff = id >= 0 ? (uint32_t)kv_row(id) * (uint32_t)C::ROWB : 0u;
         const uint32_t dst = lds_addr(buf[b & 1]);
+        if (paged) {
+            const uint8_t* src = kvb + (id >= 0 ? (uint64_t)kv_row(id) * C::ROWB : 0) + 16u * (lane >> 5);
+#pragma unroll
+            for (int u = 0; u < C::PER_W; ++u) {
+                const int i = wv + C::NW * u;
+                if (i < C::KS) dma16_at(src + 32u * i, dst + 1024u * i);
+            }
+            return;
+        }
+        const uint32_t roff = id >= 0 ? (uint32_t)id * (uint32_t)C::ROWB : 0u;
 #pragma unroll
         for (int u = 0; u < C::PER_W; ++u) {
             const int i = wv + C::NW * u;

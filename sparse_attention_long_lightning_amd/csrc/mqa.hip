@@ -170,21 +170,29 @@ __device__ __forceinline__ void piece_of(int I, int lane, int& r, int& col, int&
 
 
 // Issues the direct global->LDS loads of one block of kBlk latent rows into the buffer at
-// LDS address `buf`; `offs` points at the block's kBlk row byte offsets in LDS (empty slots
-// hold 0, i.e. row 0 of the sequence, and are zeroed by zero_empty_rows once landed).  Load
-// wave dw owns instructions I = dw + NDW*k, fixed at compile time, so the sequence is fully
-// unrolled: all offset reads first, then the loads.
-template <class C>
+// LDS address `buf`; `offs` points at the block's kBlk staged rows in LDS (empty slots hold
+// row 0, and are zeroed by zero_empty_rows once landed).  Packed caches stage byte offsets from
+// the sequence's first row (32 bits: a sequence is shorter than 2^32 / 1152 positions, checked
+// on the host) and load from the scalar base kvb; paged caches stage pool rows and load from
+// 64-bit per-lane addresses, so a page pool may exceed 4 GiB.  Load wave dw owns instructions
+// I = dw + NDW*k, fixed at compile time, so the sequence is fully unrolled: all offset reads
+// first, then the loads.
+template <class C, bool PAGED>
 __device__ __forceinline__ void issue_block(uint32_t buf, const uint8_t* kvb, const uint32_t* offs,
                                             int dw, int lane) {
     constexpr bool FULL = C::INSTRS % C::NDW == 0;  // every load wave has MAXK slots
-    uint32_t o[C::MAXK];
+    using Off = typename std::conditional<PAGED, const uint8_t*, uint32_t>::type;
+    Off o[C::MAXK];
 #pragma unroll
     for (int k = 0; k < C::MAXK; ++k) {
         const int I = dw + C::NDW * k;
         int r, col, base;
         piece_of<C>(I, lane, r, col, base);
-        o[k] = (FULL || I < C::INSTRS) ? offs[r] + col : 0u;
+        const bool live = FULL || I < C::INSTRS;
+        if constexpr (PAGED)
+            o[k] = kvb + (live ? (uint64_t)offs[r] * C::ROW_BYTES + col : 0);
+        else
+            o[k] = live ? offs[r] + col : 0u;
     }
 #pragma unroll
     for (int k = 0; k < C::MAXK; ++k) {
@@ -192,7 +200,10 @@ __device__ __forceinline__ void issue_block(uint32_t buf, const uint8_t* kvb, co
         if (FULL || I < C::INSTRS) {
             int r, col, base;
             piece_of<C>(I, lane, r, col, base);
-            dma16(kvb, o[k], buf + base);
+            if constexpr (PAGED)
+                dma16_at(o[k], buf + base);
+            else
+                dma16(kvb, o[k], buf + base);
         }
     }
 }
@@ -222,7 +233,7 @@ __device__ __forceinline__ void wait_blocks_left(int nb) {
     else wait_loads<0>();
 }
 
-template <int H, int DQK, int DV, bool SPLIT>
+template <int H, int DQK, int DV, bool SPLIT, bool PAGED>
 __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     int topk, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
@@ -267,20 +278,23 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     const int32_t* irow = dense ? nullptr : idx + (int64_t)row * topk;
     // latent rows are addressed from the sequence's first row (packed caches) or from the
     // start of the page pool (paged caches)
-    const bool paged = map.pages != nullptr;
-    const uint8_t* kvb = (const uint8_t*)(paged ? kv : kv + (int64_t)ri.kbase * DQK);
+    const uint8_t* kvb = (const uint8_t*)(PAGED ? kv : kv + (int64_t)ri.kbase * DQK);
     const int half = lane >> 5;
     const int mi = lane & 31;
     const int j16 = lane & 15;
     const uint32_t lds0 = lds_addr(lds);
 
-    // Row offsets (row 0 for an empty slot; a row's offset must fit in 32 bits) and occupancy
-    // of block b, staged in ring slot b % RING: the first RING blocks here, the rest by wave 0
-    // one step before the loads need them.
+    // Row offsets (packed: byte offset from the sequence's first row; paged: pool row) and
+    // occupancy of block b, staged in ring slot b % RING: the first RING blocks here, the rest
+    // by wave 0 one step before the loads need them.  Slots that slot_row rejects (-1, values
+    // outside the sequence, page ids outside a pool of known size) are empty: row 0 is loaded
+    // in their place and zeroed, so no load ever leaves the caches.
     auto stage = [&](int b, int id) {  // lanes 0..31 hold the ids of the block's slots
-        const uint32_t r = id < 0 ? 0u : paged ? (uint32_t)cache_row(map, ri, id) : (uint32_t)id;
-        if (lane < kBlk) rofs[b % C::RING][lane] = r * (uint32_t)C::ROW_BYTES;
-        const uint64_t m = __ballot(id >= 0);
+        const int64_t row = slot_row(map, ri, id);
+        const bool ok = row >= 0;
+        const uint32_t r = !ok ? 0u : PAGED ? (uint32_t)row : (uint32_t)id * (uint32_t)C::ROW_BYTES;
+        if (lane < kBlk) rofs[b % C::RING][lane] = r;
+        const uint64_t m = __ballot(ok);
         if (lane == 0) rmask[b % C::RING] = (uint32_t)m;
     };
     auto load_ids = [&](int b) {
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
                 const uint32_t vm = rmask[blk % C::RING];
                 if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, dw, lane);
             };
-            auto issue = [&](int blk) { issue_block<C>(buf_of(blk), kvb, rofs[blk % C::RING], dw, lane); };
+            auto issue = [&](int blk) { issue_block<C, PAGED>(buf_of(blk), kvb, rofs[blk % C::RING], dw, lane); };
             if (nblk > 0) {
                 issue(0);
                 if (nblk > 1) issue(1);
@@ -700,17 +714,18 @@ hipError_t launch_t(const MqaArgs& a, const RowMap& map, int n_rows, int n_split
                     hipStream_t st) {
     using C = MqaCfg<H, DQK, DV>;
     const float sm_log2 = a.sm_scale * 1.4426950408889634f;
+    const bool paged = map.pages != nullptr;
     if (n_split <= 1) {
-        hipLaunchKernelGGL((sparse_mqa_kernel<H, DQK, DV, false>), dim3(grid_x<C>(n_rows)), dim3(C::THREADS), 0,
-                           st, a.q, a.kv, a.idx, a.topk, a.out, a.lse, nullptr, nullptr, map, n_rows,
-                           1, sm_log2, (int)a.mode);
+        auto kern = paged ? sparse_mqa_kernel<H, DQK, DV, false, true> : sparse_mqa_kernel<H, DQK, DV, false, false>;
+        hipLaunchKernelGGL(kern, dim3(grid_x<C>(n_rows)), dim3(C::THREADS), 0, st, a.q, a.kv, a.idx, a.topk, a.out,
+                           a.lse, nullptr, nullptr, map, n_rows, 1, sm_log2, (int)a.mode);
         return hipGetLastError();
     }
     float* part_o = (float*)ws;
     float2* part_ml = (float2*)(part_o + (size_t)n_rows * n_split * H * DV);
-    hipLaunchKernelGGL((sparse_mqa_kernel<H, DQK, DV, true>), dim3(grid_x<C>(n_rows), n_split), dim3(C::THREADS),
-                       0, st, a.q, a.kv, a.idx, a.topk, a.out, a.lse, part_o, part_ml, map, n_rows,
-                       n_split, sm_log2, (int)a.mode);
+    auto kern = paged ? sparse_mqa_kernel<H, DQK, DV, true, true> : sparse_mqa_kernel<H, DQK, DV, true, false>;
+    hipLaunchKernelGGL(kern, dim3(grid_x<C>(n_rows), n_split), dim3(C::THREADS), 0, st, a.q, a.kv, a.idx, a.topk,
+                       a.out, a.lse, part_o, part_ml, map, n_rows, n_split, sm_log2, (int)a.mode);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((mqa_combine_kernel<H, DV>), dim3(n_rows, (H + 3) / 4), dim3(256), 0, st,

@@ -32,13 +32,14 @@ def rope_tables(n_pos, rope_dim, base=10000.0):
     return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
-def page_layout(lens, rng, spare=5):
+def page_layout(lens, rng, spare=5, base_page=0):
     """A shuffled page pool for sequences of the given lengths: page table [B, pps] (slots past
-    a sequence's end point at page 0, never read) and the pool row of each packed row."""
+    a sequence's end point at page 0, never read) and the pool row of each packed row.  With
+    base_page > 0 the sequences' pages are ids base_page and above of a larger pool."""
     need = [(n + PAGE - 1) // PAGE for n in lens]
     pps = max(max(need), 1)
     n_pages = sum(need) + spare
-    perm = rng.permutation(n_pages)
+    perm = rng.permutation(n_pages) + base_page
     table = np.zeros((len(lens), pps), np.int32)
     rows = []
     at = 0
@@ -47,7 +48,7 @@ def page_layout(lens, rng, spare=5):
         at += need[b]
         p = np.arange(n)
         rows.append(table[b, p // PAGE].astype(np.int64) * PAGE + p % PAGE)
-    return table, np.concatenate(rows) if rows else np.zeros(0, np.int64), n_pages * PAGE
+    return table, np.concatenate(rows) if rows else np.zeros(0, np.int64), (base_page + n_pages) * PAGE
 
 
 def append_case(dims, lens, lq, seed, dev):
@@ -152,9 +153,9 @@ def to_pool(t, row_of, n_rows, fill=0):
     return pool
 
 
-def paged_inputs(inp, seed):
+def paged_inputs(inp, seed, base_page=0):
     rng = np.random.default_rng(seed)
-    table, row_of, n_rows = page_layout(inp["lens"], rng)
+    table, row_of, n_rows = page_layout(inp["lens"], rng, base_page=base_page)
     p = dict(inp)
     p["k8"] = to_pool(inp["k8"], row_of, n_rows, 0x3C)
     p["k_scale"] = to_pool(inp["k_scale"], row_of, n_rows, 1.0)
@@ -178,14 +179,19 @@ def forward(dims, inp, dev, page_table=None):
     return out, lse, idx, sc
 
 
-@pytest.mark.parametrize("shape", ["tiny", "prod"])
-def test_paged_decode_forward_equals_packed(cuda, shape):
+# Pages from id 60,000 on: pool rows above 3.84M, i.e. latent rows more than 4 GiB into the pool
+# (1,152 bytes each), which the gathers reach through 64-bit addresses.
+HIGH_PAGE = 60000
+
+
+@pytest.mark.parametrize("shape,base_page", [("tiny", 0), ("prod", 0), ("prod", HIGH_PAGE)])
+def test_paged_decode_forward_equals_packed(cuda, shape, base_page):
     dims = dsa_inputs.TINY if shape == "tiny" else dsa_inputs.PROD
     lens = [1, 63, 64, 65, 2048, 2049, 9000, 20001] if shape == "prod" else [1, 31, 64, 65, 300, 1000]
-    say(f"paged decode forward {shape} lens {lens}")
+    say(f"paged decode forward {shape} lens {lens}, pages from id {base_page}")
     inp = dsa_inputs.decode_inputs(dims=dims, seed=5, device=cuda, lens=lens)
     ref = forward(dims, inp, cuda)
-    pinp, table = paged_inputs(inp, seed=6)
+    pinp, table = paged_inputs(inp, seed=6, base_page=base_page)
     got = forward(dims, pinp, cuda, page_table=table)
     for name, a, b in zip(("out", "lse", "idx", "scores"), ref, got):
         if name == "scores":
@@ -195,10 +201,11 @@ def test_paged_decode_forward_equals_packed(cuda, shape):
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), f"{shape} paged {name}"
 
 
-def test_paged_sparse_mqa_prefill_rows_equal_packed(cuda):
+@pytest.mark.parametrize("base_page", [0, HIGH_PAGE])
+def test_paged_sparse_mqa_prefill_rows_equal_packed(cuda, base_page):
     dims = dsa_inputs.PROD
     lens, lq = [3000, 700, 130], [40, 7, 130]
-    say(f"paged sparse MQA, several rows per sequence, lens {lens} rows {lq}")
+    say(f"paged sparse MQA, several rows per sequence, lens {lens} rows {lq}, pages from id {base_page}")
     g = torch.Generator().manual_seed(7)
     cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -215,7 +222,7 @@ def test_paged_sparse_mqa_prefill_rows_equal_packed(cuda):
             t += 1
     idx = idx.to(cuda)
     rng = np.random.default_rng(8)
-    table, row_of, n_rows = page_layout(lens, rng)
+    table, row_of, n_rows = page_layout(lens, rng, base_page=base_page)
     kvp = to_pool(kv, row_of, n_rows, 0.25)
     res = []
     for pt, cache in ((None, kv), (table, kvp)):

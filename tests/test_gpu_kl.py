@@ -95,18 +95,20 @@ def test_indexer_kl_prod(cuda, sparse):
     check_kl(rev, c["rev"], "prod KL(Q||P)")
 
 
-def test_indexer_kl_paged_equals_packed(cuda):
+@pytest.mark.parametrize("base_page", [0, 60000])
+def test_indexer_kl_paged_equals_packed(cuda, base_page):
+    # base_page 60,000: pool rows above 3.84M, latent rows more than 4 GiB into the pool
     dims = dsa_inputs.PROD
-    say("indexer KL with a paged latent cache == packed")
+    say(f"indexer KL with a paged latent cache == packed, pages from id {base_page}")
     c = case(dims, 16, 700, 3, cuda, True)
     ref = run(dims, c, cuda)
     rng = np.random.default_rng(4)
     n_pages = (700 + 63) // 64 + 3
-    perm = rng.permutation(n_pages)
+    perm = rng.permutation(n_pages) + base_page
     table = perm[: (700 + 63) // 64].astype(np.int32)[None, :]
     p = np.arange(700)
     rows = table[0, p // 64].astype(np.int64) * 64 + p % 64
-    pool = torch.zeros(n_pages * 64, dims.qk_dim, dtype=torch.bfloat16, device=cuda)
+    pool = torch.zeros((base_page + n_pages) * 64, dims.qk_dim, dtype=torch.bfloat16, device=cuda)
     pool[torch.from_numpy(rows).to(cuda)] = c["kv"]
     batch = dsa.Batch([0, 16], [0, 700], device=cuda, page_table=table)
     got = run(dims, c, cuda, batch=batch, kv=pool)
