@@ -16,7 +16,8 @@
  * ---------------------------------------
  *  - Ownership: the caller allocates every buffer (inputs, outputs, workspace) in device
  *    memory.  The library never allocates, frees or synchronises; all work is enqueued on
- *    the caller's stream.  The library keeps no mutable global state and is thread-safe.
+ *    the caller's stream.  Apart from dsa_forward_noalloc's per-device scratch array (see
+ *    there), the library keeps no mutable global state and is thread-safe.
  *  - Batches: a batch holds n_seqs sequences.  Sequence b owns query rows
  *    [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1]) of the packed arrays.  Its
  *    queries are the last len_q(b) tokens of its key sequence, so query row i of b sits at
@@ -183,6 +184,22 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
                        const float* k_scale, const uint16_t* q, const uint16_t* kv,
                        uint16_t* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/* dsa_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation with its workspace
+ * taken from a fixed array of DSA_NOALLOC_SCRATCH_BYTES bytes in the library's own device memory
+ * (one array per GPU, set up on the first call on that device and held until the process ends).
+ * The call allocates and frees nothing.  The caller still passes inputs and outputs; call it with
+ * the device of `stream` current.  Batches whose smallest workspace (dsa_workspace_min) exceeds
+ * the array return DSA_ERR_WORKSPACE before anything is enqueued; prefill passes are sized to the
+ * array.  Every call on a GPU shares that GPU's array: calls that overlap on one GPU (two streams,
+ * two threads) race and give undefined results; calls in stream order are safe.  Results equal
+ * dsa_forward's. */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dsa_status dsa_forward_noalloc(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                               const float* q_scale, const float* w, const uint8_t* k8,
+                               const float* k_scale, const uint16_t* q, const uint16_t* kv,
+                               uint16_t* out, float* lse, int32_t* idx_out, hipStream_t stream);
 
 /* Indexer training target, forward only (DeepSeek-V3.2-Exp overview, "训练": the dense
  * warm-up aligns the indexer with the main attention summed over heads and L1-normalised,

@@ -18,7 +18,8 @@ import numpy as np
 import torch
 
 __all__ = ["DsaError", "Dims", "Batch", "lib", "library_path", "indexer_scores", "topk",
-           "topk_workspace_size", "indexer_scores_counted", "topk_counted", "COUNT_BINS", "sparse_mqa", "dense_mqa", "forward", "cache_append", "indexer_kl",
+           "topk_workspace_size", "indexer_scores_counted", "topk_counted", "COUNT_BINS", "sparse_mqa", "dense_mqa", "forward", "forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "cache_append", "indexer_kl",
            "workspace_size", "workspace_min", "PROD_DIMS", "TINY_DIMS", "PAGE_SIZE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -123,6 +124,7 @@ def lib():
             "dsa_sparse_mqa": [P, P, P, P, P, P, P, P, S, P],
             "dsa_dense_mqa": [P, P, P, P, P, P, P, S, P],
             "dsa_forward": [P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
+            "dsa_forward_noalloc": [P, P, P, P, P, P, P, P, P, P, P, P, P],
             "dsa_indexer_kl": [P, P, P, P, P, P, P, I64, P, P, P],
             "dsa_cache_append": [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P],
         }.items():
@@ -245,6 +247,20 @@ def forward(dims, batch: Batch, q8, q_scale, w, k8, k_scale, q, kv, out, lse=Non
                              _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), _ptr(out),
                              _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)),
            "dsa_forward")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DSA_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(dims, batch: Batch, q8, q_scale, w, k8, k_scale, q, kv, out, lse=None, idx_out=None,
+                    stream=None):
+    """dsa_forward with the library's fixed per-device scratch array as its workspace."""
+    d = _dims(dims)
+    _check(lib().dsa_forward_noalloc(ctypes.byref(d), ctypes.byref(batch.c), _ptr(q8), _ptr(q_scale),
+                                     _ptr(w), _ptr(k8), _ptr(k_scale), _ptr(q), _ptr(kv), _ptr(out),
+                                     _ptr(lse), _ptr(idx_out), _stream(stream)),
+           "dsa_forward_noalloc")
     return out
 
 

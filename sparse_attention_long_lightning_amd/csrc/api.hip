@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstdio>
+#include <mutex>
 
 #include "dsa.h"
 #include "internal.hpp"
@@ -136,6 +137,34 @@ ForwardPlan plan_forward(const dsa_dims* d, Shape shape, const Batch& bt, int ch
 int default_chunk(const Batch& bt) {
     int c = bt.max_lq < kDefaultChunkRows ? bt.max_lq : kDefaultChunkRows;
     return c < 1 ? 1 : c;
+}
+
+}  // namespace
+
+// Workspace of dsa_forward_noalloc: one array per GPU that loads the library, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the device memory:
+// the device address is taken with hipGetSymbolAddress, once per device, and only that
+// pointer reaches kernels.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call there).
+dsa_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DSA_ERR_HIP;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return DSA_OK;
 }
 
 }  // namespace
@@ -417,6 +446,22 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
         }
     }
     return DSA_OK;
+}
+
+dsa_status dsa_forward_noalloc(const dsa_dims* dims, const dsa_batch* batch, const uint8_t* q8,
+                               const float* q_scale, const float* w, const uint8_t* k8,
+                               const float* k_scale, const uint16_t* q, const uint16_t* kv,
+                               uint16_t* out, float* lse, int32_t* idx_out, hipStream_t stream) {
+    size_t need = 0;
+    dsa_status st = dsa_workspace_min(dims, batch, &need);
+    if (st != DSA_OK) return st;
+    if (need > DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != DSA_OK) return st;
+    // dsa_forward sizes its passes to the array and clears, with kernels, every part of the
+    // workspace that must start at zero
+    return dsa_forward(dims, batch, q8, q_scale, w, k8, k_scale, q, kv, out, lse, idx_out, ws,
+                       DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 dsa_status dsa_indexer_kl(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
