@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 
 #include "dsa.h"
@@ -172,7 +173,10 @@ dsa_status scratch_of_current_device(void** out) {
 extern "C" {
 
 const char* dsa_status_string(dsa_status s) {
-    switch (s) {
+    // a caller may pass any integer; reading it as an int keeps values outside the enum defined
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
         case DSA_OK: return "DSA_OK";
         case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: invalid argument";
         case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: unsupported dims";
