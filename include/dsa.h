@@ -70,9 +70,12 @@ typedef struct {
  * of DSA_PAGE_SIZE positions (the serving setups on the DeepSeek-V3.2-Exp pages use page
  * size 64): position p of sequence b is cache row
  *     page_table_dev[b * pages_per_seq + p / 64] * 64 + p % 64
- * of the caller's page pool (page ids trusted like indices; a row offset in bytes must fit in
- * 32 bits).  Paged caches are read by the decode paths (every sequence with one query row),
- * dsa_sparse_mqa and dsa_cache_append; prefill with paged caches returns DSA_ERR_UNSUPPORTED. */
+ * of the caller's page pool of pool_rows rows.  With pool_rows > 0 the gathers treat a slot
+ * whose page lies outside the pool as empty (dsa_check_indices reports it); with pool_rows = 0
+ * page ids are trusted.  Paged caches are read by the decode paths (every sequence with one query
+ * row), dsa_sparse_mqa, dsa_indexer_kl and dsa_cache_append; prefill with paged caches returns
+ * DSA_ERR_UNSUPPORTED.  A sequence may hold at most 3,728,269 positions (2^32 bytes of latent
+ * rows); longer ones return DSA_ERR_UNSUPPORTED. */
 #define DSA_PAGE_SIZE 64
 typedef struct {
     int32_t n_seqs;                 /* B >= 1                                          */
@@ -82,6 +85,7 @@ typedef struct {
     const int32_t* cu_k_dev;        /* [B+1]                                           */
     const int32_t* page_table_dev;  /* [B, pages_per_seq] page ids, or NULL (packed)    */
     int32_t pages_per_seq;          /* >= ceil(max len_k / 64) when paged               */
+    int64_t pool_rows;              /* rows in the page pool, or 0 (not given)          */
 } dsa_batch;
 
 /* Bytes of workspace that dsa_forward uses by default for this batch (also enough for
@@ -147,8 +151,9 @@ dsa_status dsa_topk_counted(const dsa_dims* dims, const dsa_batch* batch, const 
                             int64_t score_stride, const uint32_t* counts, int32_t* idx, hipStream_t stream);
 
 /* Sparse MQA over the latent cache (stage 3).
- * For query row i and head h, over the slots of idx[i,:] that are not -1 (positions in
- * the row's own sequence; trusted to lie in [0, len_k)):
+ * For query row i and head h, over the slots of idx[i,:] that hold a position of the row's
+ * own sequence, i.e. a value in [0, len_k) (-1 marks an empty slot; any other value is treated
+ * as empty too and never loaded; dsa_check_indices reports such rows):
  *   z_s = sm_scale * q[i,h,:qk_dim] . kv[s,:qk_dim]
  *   out[i,h,:] = sum_s softmax(z)_s * kv[s,:v_dim],   lse[i,h] = ln sum_s exp(z_s)
  * Every head reads the same latent rows (MQA mode).  A row without valid slots gets
@@ -243,6 +248,33 @@ dsa_status dsa_cache_append(const dsa_dims* dims, const dsa_batch* batch, const 
                             const float* rope_sin, int32_t n_pos, uint8_t* q8, float* q_scale,
                             uint8_t* k8_cache, float* k_scale_cache, uint16_t* kv_cache,
                             hipStream_t stream);
+
+/* Index-row check (the selected positions are the attention's gather addresses: lightning-
+ * indexer walk-through, step 4).  For each query row i of the batch, row_flags[i] (uint32,
+ * device memory) receives the OR of:
+ *   DSA_IDX_OUT_OF_RANGE  an entry below -1 or >= len_k of the row's sequence
+ *   DSA_IDX_NOT_CAUSAL    an entry in (p_i, len_k): past the query's own position
+ *   DSA_IDX_NOT_SORTED    valid entries not strictly ascending, or a valid entry after a -1
+ *                         (the form dsa_topk writes; dsa_sparse_mqa accepts any order)
+ *   DSA_IDX_BAD_PAGE      paged caches with pool_rows > 0: an entry whose page lies outside the
+ *                         pool
+ * 0 for a row that dsa_topk could have written.  The gathers of dsa_sparse_mqa and
+ * dsa_indexer_kl treat out-of-range entries and bad pages as empty slots, so such rows never
+ * make them read outside the caches; this call says whether a row had any.
+ *   idx [T, topk] int32 (16-byte aligned), row_flags [T] uint32. */
+#define DSA_IDX_OUT_OF_RANGE 1u
+#define DSA_IDX_NOT_CAUSAL 2u
+#define DSA_IDX_NOT_SORTED 4u
+#define DSA_IDX_BAD_PAGE 8u
+dsa_status dsa_check_indices(const dsa_dims* dims, const dsa_batch* batch, const int32_t* idx,
+                             uint32_t* row_flags, hipStream_t stream);
+
+/* Debug checks.  With the environment variable DSA_DEBUG_CHECKS=1 (read at every call),
+ * dsa_sparse_mqa, dsa_indexer_kl and dsa_forward run the check above on every index row before
+ * their gathers read it and OR the flags into a per-device word.  dsa_debug_flags copies the
+ * current device's word to *flags (host memory; waits for the device) and clears it when clear
+ * is non-zero.  Without the variable the word stays 0 and nothing extra is launched. */
+dsa_status dsa_debug_flags(uint32_t* flags, int clear);
 
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status status);

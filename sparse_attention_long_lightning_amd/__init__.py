@@ -19,6 +19,7 @@ import torch
 
 __all__ = ["DsaError", "Dims", "Batch", "lib", "library_path", "indexer_scores", "topk",
            "topk_workspace_size", "indexer_scores_counted", "topk_counted", "COUNT_BINS", "sparse_mqa", "dense_mqa", "forward", "forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "check_indices", "debug_flags", "IDX_OUT_OF_RANGE", "IDX_NOT_CAUSAL", "IDX_NOT_SORTED", "IDX_BAD_PAGE",
            "cache_append", "indexer_kl",
            "workspace_size", "workspace_min", "PROD_DIMS", "TINY_DIMS", "PAGE_SIZE", "STATUS"]
 
@@ -51,7 +52,7 @@ class _CBatch(ctypes.Structure):
     _fields_ = [("n_seqs", ctypes.c_int32), ("cu_q_host", ctypes.c_void_p),
                 ("cu_k_host", ctypes.c_void_p), ("cu_q_dev", ctypes.c_void_p),
                 ("cu_k_dev", ctypes.c_void_p), ("page_table_dev", ctypes.c_void_p),
-                ("pages_per_seq", ctypes.c_int32)]
+                ("pages_per_seq", ctypes.c_int32), ("pool_rows", ctypes.c_int64)]
 
 
 PAGE_SIZE = 64  # positions per cache page (DSA_PAGE_SIZE)
@@ -61,9 +62,10 @@ class Batch:
     """Sequence offsets in host and device memory, kept alive together.
 
     page_table: optional int32 array [B, pages_per_seq] of page ids; the caches are then paged
-    (position p of sequence b is cache row page_table[b, p // 64] * 64 + p % 64)."""
+    (position p of sequence b is cache row page_table[b, p // 64] * 64 + p % 64) in a pool of
+    pool_rows rows (0: not given; the gathers then trust the page ids)."""
 
-    def __init__(self, cu_q, cu_k, device="cuda", page_table=None):
+    def __init__(self, cu_q, cu_k, device="cuda", page_table=None, pool_rows=0):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int32))
         self.cu_k = np.ascontiguousarray(np.asarray(cu_k, dtype=np.int32))
         if self.cu_q.shape != self.cu_k.shape or self.cu_q.ndim != 1 or len(self.cu_q) < 2:
@@ -80,7 +82,8 @@ class Batch:
             pps = int(pt.shape[1])
         self.c = _CBatch(len(self.cu_q) - 1, self.cu_q.ctypes.data, self.cu_k.ctypes.data,
                          self.cu_q_dev.data_ptr(), self.cu_k_dev.data_ptr(),
-                         None if self.page_table_dev is None else self.page_table_dev.data_ptr(), pps)
+                         None if self.page_table_dev is None else self.page_table_dev.data_ptr(), pps,
+                         int(pool_rows))
 
     @property
     def n_seqs(self) -> int:
@@ -125,6 +128,8 @@ def lib():
             "dsa_dense_mqa": [P, P, P, P, P, P, P, S, P],
             "dsa_forward": [P, P, P, P, P, P, P, P, P, P, P, P, P, S, P],
             "dsa_forward_noalloc": [P, P, P, P, P, P, P, P, P, P, P, P, P],
+            "dsa_check_indices": [P, P, P, P, P],
+            "dsa_debug_flags": [P, ctypes.c_int],
             "dsa_indexer_kl": [P, P, P, P, P, P, P, I64, P, P, P],
             "dsa_cache_append": [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P],
         }.items():
@@ -248,6 +253,24 @@ def forward(dims, batch: Batch, q8, q_scale, w, k8, k_scale, q, kv, out, lse=Non
                              _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)),
            "dsa_forward")
     return out
+
+
+IDX_OUT_OF_RANGE, IDX_NOT_CAUSAL, IDX_NOT_SORTED, IDX_BAD_PAGE = 1, 2, 4, 8  # DSA_IDX_* row flags
+
+
+def check_indices(dims, batch: Batch, idx, row_flags, stream=None):
+    """Flags of each index row (DSA_IDX_* bits, 0 for a row dsa_topk could have written)."""
+    d = _dims(dims)
+    _check(lib().dsa_check_indices(ctypes.byref(d), ctypes.byref(batch.c), _ptr(idx), _ptr(row_flags),
+                                   _stream(stream)), "dsa_check_indices")
+    return row_flags
+
+
+def debug_flags(clear: bool = True) -> int:
+    """The current device's DSA_DEBUG_CHECKS flag word (waits for the device)."""
+    out = ctypes.c_uint32(0)
+    _check(lib().dsa_debug_flags(ctypes.byref(out), int(clear)), "dsa_debug_flags")
+    return int(out.value)
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # DSA_NOALLOC_SCRATCH_BYTES

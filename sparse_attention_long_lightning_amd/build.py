@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdsa.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mqa.hip", "cache.hip", "kl.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mqa.hip", "cache.hip", "kl.hip", "check.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 arithmetic is disabled for every HIP translation unit (hipcc otherwise forms

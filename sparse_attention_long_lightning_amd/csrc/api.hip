@@ -31,10 +31,17 @@ struct Batch {
     bool decode = false;  // every sequence has exactly one query row
     const int32_t* pages = nullptr;  // paged caches (device page table) or nullptr
     int pages_per_seq = 0;
+    int64_t pool_rows = 0;           // rows of the page pool (0: not given)
     const dsa_batch* raw = nullptr;
+    RowMap map() const {
+        return RowMap{raw->cu_q_dev, raw->cu_k_dev, B, 0, 0, 0, pages, pages_per_seq, pool_rows};
+    }
     int lq(int b) const { return raw->cu_q_host[b + 1] - raw->cu_q_host[b]; }
     int lk(int b) const { return raw->cu_k_host[b + 1] - raw->cu_k_host[b]; }
 };
+
+// Sequences are addressed with 32-bit byte offsets of 1152-byte latent rows from their first row.
+constexpr int64_t kMaxLenK = (int64_t(1) << 32) / 1152 - 1;
 
 bool debug_log() {
     static const bool on = [] {
@@ -74,6 +81,7 @@ dsa_status check_batch(const dsa_batch* b, Batch* out) {
         const int64_t lq = (int64_t)b->cu_q_host[i + 1] - b->cu_q_host[i];
         const int64_t lk = (int64_t)b->cu_k_host[i + 1] - b->cu_k_host[i];
         if (lq < 0 || lk < 0 || lq > lk) return DSA_ERR_INVALID_ARG;
+        if (lk > kMaxLenK) return DSA_ERR_UNSUPPORTED;
         if (lq > r.max_lq) r.max_lq = (int)lq;
         if (lk > r.max_lk) r.max_lk = (int)lk;
         if (lq != 1) r.decode = false;
@@ -81,9 +89,11 @@ dsa_status check_batch(const dsa_batch* b, Batch* out) {
     r.T = b->cu_q_host[b->n_seqs];
     r.S = b->cu_k_host[b->n_seqs];
     if (b->page_table_dev != nullptr) {
-        if (b->pages_per_seq < 1 || (int64_t)b->pages_per_seq * kPage < r.max_lk) return DSA_ERR_INVALID_ARG;
+        if (b->pages_per_seq < 1 || (int64_t)b->pages_per_seq * kPage < r.max_lk || b->pool_rows < 0)
+            return DSA_ERR_INVALID_ARG;
         r.pages = b->page_table_dev;
         r.pages_per_seq = b->pages_per_seq;
+        r.pool_rows = b->pool_rows;
     }
     *out = r;
     return DSA_OK;
@@ -142,6 +152,10 @@ int default_chunk(const Batch& bt) {
 
 }  // namespace
 
+// Flags that DSA_DEBUG_CHECKS=1 collects from every index row a gather reads (the OR of the
+// checker's row flags), per device; read and cleared by dsa_debug_flags.
+static __device__ uint32_t debug_flags;
+
 // Workspace of dsa_forward_noalloc: one array per GPU that loads the library, held until the
 // process ends.  In host code `scratch` names a host-side stand-in, never the device memory:
 // the device address is taken with hipGetSymbolAddress, once per device, and only that
@@ -153,6 +167,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_dev[kMaxDevices] = {};
+uint32_t* g_debug_dev[kMaxDevices] = {};
 
 // Device address of the current device's scratch array (looked up on the first call there).
 dsa_status scratch_of_current_device(void** out) {
@@ -166,6 +181,35 @@ dsa_status scratch_of_current_device(void** out) {
     }
     *out = g_scratch_dev[dev];
     return DSA_OK;
+}
+
+// Device address of the current device's debug flag word.
+dsa_status debug_word_of_current_device(uint32_t** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_debug_dev[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(debug_flags)) != hipSuccess || p == nullptr) return DSA_ERR_HIP;
+        g_debug_dev[dev] = (uint32_t*)p;
+    }
+    *out = g_debug_dev[dev];
+    return DSA_OK;
+}
+
+// Read on every call, so that a process can switch the checks on and off.
+bool debug_checks() {
+    const char* e = getenv("DSA_DEBUG_CHECKS");
+    return e != nullptr && e[0] == '1';
+}
+
+// With DSA_DEBUG_CHECKS=1: checks the index rows a gather is about to read and ORs their flags
+// into the device's debug word (a no-op otherwise).
+hipError_t debug_check(const int32_t* idx, int topk, const RowMap& map, int n_rows, hipStream_t st) {
+    if (!debug_checks() || idx == nullptr) return hipSuccess;
+    uint32_t* word = nullptr;
+    if (debug_word_of_current_device(&word) != DSA_OK) return hipErrorInvalidValue;
+    return launch_check_indices(idx, topk, map, n_rows, nullptr, word, st);
 }
 
 }  // namespace
@@ -281,7 +325,7 @@ dsa_status dsa_topk_counted(const dsa_dims* dims, const dsa_batch* batch, const 
     if (!scores || !idx || !counts || !aligned16(scores) || !aligned16(idx) || !aligned16(counts))
         return DSA_ERR_INVALID_ARG;
     if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
-    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0};
+    const RowMap map = bt.map();
     return hip_status(launch_topk_from_hist(scores, score_stride, counts, idx, dims->topk, map, bt.T, stream));
 }
 
@@ -307,7 +351,7 @@ dsa_status dsa_topk(const dsa_dims* dims, const dsa_batch* batch, const float* s
     if (!scores || !idx || !aligned16(scores) || !aligned16(idx)) return DSA_ERR_INVALID_ARG;
     if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
     if (ws != nullptr && !aligned16(ws)) return DSA_ERR_WORKSPACE;
-    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
+    const RowMap map = bt.map();
     return hip_status(launch_topk(scores, score_stride, idx, dims->topk, map, bt.T, bt.max_lk, ws,
                                   ws == nullptr ? 0 : ws_bytes, stream));
 }
@@ -329,8 +373,10 @@ dsa_status dsa_sparse_mqa(const dsa_dims* dims, const dsa_batch* batch, const ui
     const size_t need = mqa_split_bytes(shape, bt.T, n_split);
     if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return DSA_ERR_WORKSPACE;
     MqaArgs a{shape, q, kv, idx, dims->topk, out, lse, dims->sm_scale};
-    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
-    return hip_status(launch_sparse_mqa(a, map, bt.T, n_split, ws, stream));
+    const RowMap map = bt.map();
+    hipError_t e = debug_check(idx, dims->topk, map, bt.T, stream);
+    if (e == hipSuccess) e = launch_sparse_mqa(a, map, bt.T, n_split, ws, stream);
+    return hip_status(e);
 }
 
 dsa_status dsa_dense_mqa(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
@@ -349,7 +395,7 @@ dsa_status dsa_dense_mqa(const dsa_dims* dims, const dsa_batch* batch, const uin
     const size_t need = mqa_split_bytes(shape, bt.T, n_split);
     if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return DSA_ERR_WORKSPACE;
     MqaArgs a{shape, q, kv, nullptr, dims->topk, out, lse, dims->sm_scale, IdxMode::Dense};
-    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
+    const RowMap map = bt.map();
     return hip_status(launch_sparse_mqa(a, map, bt.T, n_split, ws, stream));
 }
 
@@ -380,7 +426,7 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
         float* sc = (float*)(wsb + p.scores_off);
         int32_t* ix = idx_out ? idx_out : (int32_t*)(wsb + p.idx_off);
         IndexerArgs ia{shape, q8, q_scale, w, k8, k_scale, sc, p.stride};
-        RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
+        const RowMap map = bt.map();
         const int n_split = mqa_splits(bt.T, topk);
         // the top-k rows hold their valid slots first: short rows read only p + 1 of them
         MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale, IdxMode::Front};
@@ -396,6 +442,7 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
         if (e == hipSuccess)
             e = launch_topk_list(sc, p.stride, hs, ix, topk, map, bt.T, bt.max_lk, hs + (size_t)bt.T * kHistBins,
                                  stream);
+        if (e == hipSuccess) e = debug_check(ix, topk, map, bt.T, stream);
         if (e == hipSuccess) e = launch_sparse_mqa(ma, map, bt.T, n_split, wsb + p.tail_off, stream);
         return hip_status(e);
     }
@@ -445,6 +492,7 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
             if (e == hipSuccess && (!dense || idx_out != nullptr))
                 e = launch_topk_from_hist(sc, p.stride, hs, ix, topk, map, r1 - r0, stream);
             MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale, dense ? IdxMode::Dense : IdxMode::Front};
+            if (e == hipSuccess && !dense) e = debug_check(ix, topk, map, r1 - r0, stream);
             if (e == hipSuccess) e = launch_sparse_mqa(ma, map, r1 - r0, 1, nullptr, stream);
             if (e != hipSuccess) return DSA_ERR_HIP;
         }
@@ -468,6 +516,28 @@ dsa_status dsa_forward_noalloc(const dsa_dims* dims, const dsa_batch* batch, con
                        DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+dsa_status dsa_check_indices(const dsa_dims* dims, const dsa_batch* batch, const int32_t* idx,
+                             uint32_t* row_flags, hipStream_t stream) {
+    Shape shape;
+    Batch bt;
+    dsa_status st;
+    if ((st = check_dims(dims, &shape)) != DSA_OK) return st;
+    if ((st = check_batch(batch, &bt)) != DSA_OK) return st;
+    if (bt.T == 0) return DSA_OK;
+    if (!idx || !row_flags || !aligned16(idx) || !aligned16(row_flags)) return DSA_ERR_INVALID_ARG;
+    return hip_status(launch_check_indices(idx, dims->topk, bt.map(), bt.T, row_flags, nullptr, stream));
+}
+
+dsa_status dsa_debug_flags(uint32_t* flags, int clear) {
+    if (flags == nullptr) return DSA_ERR_INVALID_ARG;
+    uint32_t* word = nullptr;
+    dsa_status st = debug_word_of_current_device(&word);
+    if (st != DSA_OK) return st;
+    if (hipMemcpy(flags, word, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return DSA_ERR_HIP;
+    if (clear && hipMemset(word, 0, sizeof(uint32_t)) != hipSuccess) return DSA_ERR_HIP;
+    return DSA_OK;
+}
+
 dsa_status dsa_indexer_kl(const dsa_dims* dims, const dsa_batch* batch, const uint16_t* q,
                           const uint16_t* kv, const float* lse, const int32_t* idx, const float* scores,
                           int64_t score_stride, float* kl, float* kl_rev, hipStream_t stream) {
@@ -484,8 +554,10 @@ dsa_status dsa_indexer_kl(const dsa_dims* dims, const dsa_batch* batch, const ui
     if (score_stride < bt.max_lk || (score_stride & 3) != 0) return DSA_ERR_INVALID_ARG;
     KlArgs a{shape, q, kv, lse, idx, dims->topk, idx ? IdxMode::General : IdxMode::Dense, scores, score_stride,
              kl, kl_rev, dims->sm_scale};
-    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
-    return hip_status(launch_indexer_kl(a, map, bt.T, stream));
+    const RowMap map = bt.map();
+    hipError_t e = debug_check(idx, dims->topk, map, bt.T, stream);
+    if (e == hipSuccess) e = launch_indexer_kl(a, map, bt.T, stream);
+    return hip_status(e);
 }
 
 dsa_status dsa_cache_append(const dsa_dims* dims, const dsa_batch* batch, const float* q_idx,
@@ -507,7 +579,7 @@ dsa_status dsa_cache_append(const dsa_dims* dims, const dsa_batch* batch, const 
         (kv_new != nullptr && (!aligned16(kv_new) || !aligned16(kv_cache))))
         return DSA_ERR_INVALID_ARG;
     if (n_pos < bt.max_lk) return DSA_ERR_INVALID_ARG;  // every new position has a table row
-    RowMap map{batch->cu_q_dev, batch->cu_k_dev, bt.B, 0, 0, 0, bt.pages, bt.pages_per_seq};
+    const RowMap map = bt.map();
     CacheAppendArgs a{shape, q_idx, k_idx, kv_new, rope_cos, rope_sin, q8, q_scale, k8_cache, k_scale_cache, kv_cache};
     return hip_status(launch_cache_append(a, map, bt.T, stream));
 }

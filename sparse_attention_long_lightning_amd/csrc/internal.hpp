@@ -120,6 +120,16 @@ struct KlArgs {
     float sm_scale;
 };
 
+// Flags of an index row (the values of DSA_IDX_* in dsa.h).
+constexpr uint32_t kIdxOutOfRange = 1u;  // an entry below -1 or past the sequence
+constexpr uint32_t kIdxNotCausal = 2u;   // an entry past the query's own position
+constexpr uint32_t kIdxNotSorted = 4u;   // valid entries not strictly ascending before the -1 pads
+constexpr uint32_t kIdxBadPage = 8u;     // paged caches: an entry's page lies outside the pool
+// Checks n_rows index rows (row i at idx + i * topk): row_flags[i] (if given) receives the OR
+// of the row's flags, and every non-zero row ORs them into *any_flags (if given).
+hipError_t launch_check_indices(const int32_t* idx, int topk, const RowMap& map, int n_rows, uint32_t* row_flags,
+                                uint32_t* any_flags, hipStream_t st);
+
 // KL divergences between the heads-summed attention distribution and the indexer's softmax
 // over each row's slots (one workgroup per row).
 hipError_t launch_indexer_kl(const KlArgs& a, const RowMap& map, int n_rows, hipStream_t st);

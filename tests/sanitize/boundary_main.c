@@ -153,6 +153,22 @@ int main(void) {
     EXPECT(dsa_forward_noalloc(&d, &big.b, F, F, F, F, F, F, F, F, NULL, NULL, NULL), DSA_ERR_WORKSPACE);
     EXPECT(dsa_forward_noalloc(&x, &pre.b, F, F, F, F, F, F, F, F, NULL, NULL, NULL), DSA_ERR_UNSUPPORTED);
 
+    /* index check and debug flags */
+    EXPECT(dsa_check_indices(&d, &pre.b, NULL, F, NULL), DSA_ERR_INVALID_ARG);
+    EXPECT(dsa_check_indices(&d, &pre.b, F, M, NULL), DSA_ERR_INVALID_ARG);
+    EXPECT(dsa_check_indices(&x, &pre.b, F, F, NULL), DSA_ERR_UNSUPPORTED);
+    EXPECT(dsa_debug_flags(NULL, 1), DSA_ERR_INVALID_ARG);
+    /* a page pool of negative size; a sequence past 32-bit latent row offsets */
+    const int32_t oq[2] = {0, 1}, ok_[2] = {0, 3728270};
+    host_batch lng;
+    make(&lng, 1, oq, ok_);
+    EXPECT(fwd(&d, &lng.b, F, F, hi), DSA_ERR_UNSUPPORTED);
+    make(&pg, 2, gq, gk);
+    pg.b.page_table_dev = (const int32_t*)F;
+    pg.b.pages_per_seq = 5;
+    pg.b.pool_rows = -64;
+    EXPECT(fwd(&d, &pg.b, F, F, hi), DSA_ERR_INVALID_ARG);
+
     /* status strings */
     for (int s = 0; s <= 4; ++s)
         if (dsa_status_string((dsa_status)s) == NULL || strncmp(dsa_status_string((dsa_status)s), "DSA_", 4) != 0)

@@ -225,3 +225,30 @@ def test_counted_stages_reject_bad_arguments():
     assert lib.dsa_topk_counted(ctypes.byref(d), ctypes.byref(b.c), FAKE, 64, None, FAKE, None) == INVALID
     assert lib.dsa_topk_counted(ctypes.byref(d), ctypes.byref(b.c), FAKE, 64, FAKE, None, None) == INVALID
     assert lib.dsa_topk_counted(ctypes.byref(d), ctypes.byref(b.c), FAKE, 60, FAKE, FAKE, None) == INVALID
+
+
+def test_index_check_and_debug_flags_reject_bad_arguments():
+    d, b = dims_with(), cpu_batch([0, 4], [0, 100])
+    lib = dsa.lib()
+    assert lib.dsa_check_indices(ctypes.byref(d), ctypes.byref(b.c), None, FAKE, None) == INVALID
+    assert lib.dsa_check_indices(ctypes.byref(d), ctypes.byref(b.c), FAKE, None, None) == INVALID
+    assert lib.dsa_check_indices(ctypes.byref(d), ctypes.byref(b.c), FAKE + 4, FAKE, None) == INVALID
+    assert lib.dsa_check_indices(ctypes.byref(dims_with(qk_dim=512)), ctypes.byref(b.c), FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.dsa_check_indices(ctypes.byref(d), ctypes.byref(cpu_batch([0, 0], [0, 9]).c), None, None, None) == OK
+    assert lib.dsa_debug_flags(None, 0) == INVALID
+
+
+def test_sequences_past_the_32_bit_row_offsets_are_unsupported():
+    # latent rows are addressed by 32-bit byte offsets from a sequence's first row
+    d = dims_with()
+    longest = (1 << 32) // 1152 - 1
+    assert call_forward(d, cpu_batch([0, 1], [0, longest])) != UNSUPPORTED
+    assert call_forward(d, cpu_batch([0, 1], [0, longest + 1])) == UNSUPPORTED
+
+
+def test_negative_pool_size_is_invalid():
+    d = dims_with()
+    b = dsa.Batch([0, 1], [0, 100], device="cpu", page_table=np.zeros((1, 2), np.int32), pool_rows=128)
+    assert b.c.pool_rows == 128
+    b.c.pool_rows = -1
+    assert call_forward(d, b) == INVALID
