@@ -63,6 +63,7 @@ def lib():
         L.orc_cache_append.argtypes = [I, I, I, P, P, P, P, P, I64, I, P, P, P, P]
         L.orc_indexer_kl.argtypes = [I, I, D, I, P, P, P, I, P, P, I64, P, P]
         L.orc_num_threads.restype = I
+        L.orc_set_num_threads.argtypes = [I]
         _lib = L
     return _lib
 
@@ -74,6 +75,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---- codecs ---------------------------------------------------------------------------

@@ -502,6 +502,16 @@ void orc_indexer_kl(int H, int Dqk, double sm, int T, const uint16_t* q, const u
     }
 }
 
+/* Threads used by the OpenMP loops from now on (the benchmark times the oracle on one core
+ * as well as on all of them). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -1,4 +1,5 @@
-"""Builds ``libdsa.so`` (the C-ABI DSA library, HIP kernels for gfx950) in-tree with hipcc.
+"""Builds ``libdsa.so`` (the C-ABI DSA library, HIP kernels for gfx950) and ``libpeak.so`` (the
+device peak probes the benchmark divides by) in-tree with hipcc.
 
 Usage: ``python -m sparse_attention_long_lightning_amd.build`` (also run by the repository's
 ``__graft_entry__.build()``).
@@ -15,6 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdsa.so")
+PEAK_LIB = os.path.join(HERE, "libpeak.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mqa.hip", "cache.hip", "kl.hip", "check.hip"]
 ARCH = "gfx950"
@@ -53,8 +55,12 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     # --no-undefined: a kernel whose host stub was not emitted fails here, not at load time
     _run(["hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # the peak probes the benchmark divides by (not part of the attention path)
+    tmp = PEAK_LIB + ".tmp"
+    _run(["hipcc", *HIP_FLAGS, "-shared", "-o", tmp, os.path.join(CSRC, "peak.hip")])
+    os.replace(tmp, PEAK_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PEAK_LIB)
     return LIB
 
 
