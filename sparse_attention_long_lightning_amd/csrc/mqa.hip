@@ -19,7 +19,7 @@
 //               B = the query heads of one 32-head group, kept in registers) over the first
 //               half of the 576 dims; then the sum with the other half, masking, the base-2
 //               online softmax (lane l owns head l % 32; O is rescaled only when a block max
-//               exceeds the running max by more than 16) and P^T published to LDS;
+//               exceeds the running max by more than 64) and P^T published to LDS;
 //   waves 4, 5  the other half of the same group's logits, handed over through LDS and
 //               computed one block ahead, so their MFMAs run beside the softmax of waves 0, 1
 //               on the same SIMD; they also issue the direct global->LDS loads of the block
@@ -38,7 +38,14 @@ namespace dsa {
 namespace {
 
 constexpr int kBlk = 32;            // selected rows per LDS block
-constexpr float kRescaleGap = 16.f;  // base-2 headroom before O is rescaled
+// Base-2 headroom of the lazy running max before O is rescaled.  A rescale costs the value
+// waves ~2,000 cycles (their 128 accumulator AGPRs pass through VGPRs), and each one is taken
+// for a whole wave of 64 heads, so a small gap rescales at almost every block once the heads
+// meet their large logits in different blocks.  With the running max at most 64 below the
+// true max, p <= 2^64, l <= n * 2^64 and |O| <= n * 2^64 * max|v| stay finite in fp32 for
+// n <= 2^17 slots and |v| < 2^47; terms the lag pushes below fp32's range are below 2^-126 of
+// the largest p, which is at least 1.
+constexpr float kRescaleGap = 64.f;
 
 // One region (value part or rope part) of the LDS image of a block: kBlk rows of NC 16-byte
 // chunks, written 1 KiB (64 chunks) per direct-load instruction.

@@ -2,7 +2,7 @@
 
 The kernel keeps a running maximum of the base-2 logits per head and rescales its output
 accumulators (hand-written AGPR code with fixed hazard waits) only when a block of 32 slots
-brings a maximum more than 16 above it.  Here every head's logits follow a chosen pattern so
+brings a maximum more than 64 above it.  Here every head's logits follow a chosen pattern so
 that the rescale branch is taken, skipped at the gap, taken in the first and in the last block,
 after empty blocks and from very negative starts; the output and lse must still match the
 oracle's softmax (DeepSeek-V3.2 explained, section 二.1: attention of the query over the
@@ -37,14 +37,14 @@ def patterns(n_slots, rng):
     nb = int(b.max()) + 1
     u = rng.uniform
     y = np.zeros((8, n_slots))
-    y[0] = np.where(b < 8, 17.0 * b, 17.0 * 7 - 30.0) + u(-2, 0, n_slots)          # +17 each block
-    y[1] = np.where(b < 6, 16.0 * b, 80.0) + np.where(b % 2 == 0, -0.05, 0.05) * (b < 6)  # ~16 steps
-    y[2] = np.where(b == nb - 1, 45.0, 0.0) + u(-5, 5, n_slots) * (b != nb - 1)     # jump in the last block
+    y[0] = np.where(b < 8, 65.0 * b, 65.0 * 7 - 100.0) + u(-2, 0, n_slots)         # +65 each block
+    y[1] = np.where(b < 6, 64.0 * b, 320.0) + np.where(b % 2 == 0, -0.05, 0.05) * (b < 6)  # ~64 steps
+    y[2] = np.where(b == nb - 1, 90.0, 0.0) + u(-5, 5, n_slots) * (b != nb - 1)     # jump in the last block
     y[3] = -10.0 * b + u(-3, 0, n_slots)                                            # decreasing
-    y[4] = rng.normal(0, 30, n_slots)                                               # many rescales
+    y[4] = rng.normal(0, 120, n_slots)                                              # many rescales
     y[5] = np.where(b == 0, -100.0, np.where(b == 1, -140.0, u(0, 1, n_slots)))     # very negative start
     y[6] = 3.0                                                                      # constant
-    y[7] = np.where(b >= 1, 17.0, 0.0) + u(-0.5, 0, n_slots)                        # one jump at block 1
+    y[7] = np.where(b >= 1, 65.0, 0.0) + u(-0.5, 0, n_slots)                        # one jump at block 1
     return y
 
 
