@@ -34,7 +34,7 @@ struct Batch {
     int64_t pool_rows = 0;           // rows of the page pool (0: not given)
     const dsa_batch* raw = nullptr;
     RowMap map() const {
-        return RowMap{raw->cu_q_dev, raw->cu_k_dev, B, 0, 0, 0, pages, pages_per_seq, pool_rows};
+        return RowMap{raw->cu_q_dev, raw->cu_k_dev, B, 0, 0, 0, pages, pages_per_seq, pool_rows, decode};
     }
     int lq(int b) const { return raw->cu_q_host[b + 1] - raw->cu_q_host[b]; }
     int lk(int b) const { return raw->cu_k_host[b + 1] - raw->cu_k_host[b]; }

@@ -24,6 +24,8 @@ constexpr int kMaxTopk = 8192;  // largest k accepted (k = 2048 in the DeepSeek-
 //  paged caches (pages != nullptr): position p of sequence s is cache row
 //      pages[s * pages_per_seq + p / kPage] * kPage + p % kPage
 //  of a pool of pool_rows rows (0: not given, page ids are then trusted).
+//  one_row_per_seq (batch mode, set by the host only when every sequence has exactly one
+//      query row, so cu_q[b] = b): row i is sequence i, found without searching cu_q.
 struct RowMap {
     const int32_t* cu_q;
     const int32_t* cu_k;
@@ -34,6 +36,7 @@ struct RowMap {
     const int32_t* pages = nullptr;
     int pages_per_seq = 0;
     int64_t pool_rows = 0;
+    bool one_row_per_seq = false;
 };
 
 constexpr int kPage = 64;  // positions per cache page
@@ -63,16 +66,24 @@ __device__ __forceinline__ RowInfo row_info(const RowMap& m, int i) {
         r.lim = r.pos;
         return r;
     }
-    int lo = 0, hi = m.n_seqs - 1;  // last b with cu_q[b] <= i
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (m.cu_q[mid] <= i) lo = mid; else hi = mid - 1;
+    int b, lq, q0;
+    if (m.one_row_per_seq) {  // decode batches: no chain of dependent loads through cu_q
+        b = i;
+        lq = 1;
+        q0 = i;
+    } else {
+        int lo = 0, hi = m.n_seqs - 1;  // last b with cu_q[b] <= i
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (m.cu_q[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        q0 = m.cu_q[b];
+        lq = m.cu_q[b + 1] - q0;
     }
-    int b = lo;
-    int lq = m.cu_q[b + 1] - m.cu_q[b];
-    int lk = m.cu_k[b + 1] - m.cu_k[b];
+    const int lk = m.cu_k[b + 1] - m.cu_k[b];
     r.qrow = i;
-    r.pos = lk - lq + (i - m.cu_q[b]);
+    r.pos = lk - lq + (i - q0);
     r.kbase = m.cu_k[b];
     r.seq = b;
     r.lim = lk - 1;
