@@ -390,48 +390,99 @@ struct SelSmem {
     int wsum[kWaves];
     int wgt[kWaves], weq[kWaves];
     int sel_bin, sel_above;
+    int wcnt[2];
 };
 
 // Among keys[0..m) in LDS, the kk-th largest key theta (1 <= kk <= m) and the number of
 // keys above it.  Radix select over the keys' actual range [lo, hi]: each pass splits the
 // current range into 2048 bins (11 bits of key - lo), so at most three passes reach a
 // single key value.  keys must hold m rounded up to a multiple of 4 entries (16-byte reads).
+// A caller that knows the range holding theta passes it as [lo_hint, lo_hint + lim_hint]:
+// the first pass then histograms that range directly and counts the keys above it, with no
+// pass for the keys' extent.  If some key lies below the range, or theta is not in it, the
+// hint is dropped and the general search runs.
 __device__ void lds_kth_key(const uint32_t* keys, int m, int kk, SelSmem& sm, uint32_t& theta,
-                            int& above) {
+                            int& above, uint32_t lo_hint = 0u, uint32_t lim_hint = 0xffffffffu) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint4* k4 = (const uint4*)keys;
     const int m4 = (m + 3) >> 2;
-    uint32_t lo = 0xffffffffu, hi = 0u;
-    for (int i = tid; i < m4; i += kThreads) {
-        const uint4 v = k4[i];
-        const uint32_t k[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (4 * i + c < m) {
-                lo = min(lo, k[c]);
-                hi = max(hi, k[c]);
-            }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-    }
-    if (lane == 0) {
-        sm.wgt[wv] = (int)lo;
-        sm.weq[wv] = (int)hi;
-    }
-    __syncthreads();
-    lo = 0xffffffffu;
-    hi = 0u;
-    for (int w = 0; w < kWaves; ++w) {
-        lo = min(lo, (uint32_t)sm.wgt[w]);
-        hi = max(hi, (uint32_t)sm.weq[w]);
-    }
-    __syncthreads();
-    // the kk-th key lies in [lo, lo + lim]; `ab` keys lie above that range
-    uint32_t lim = hi - lo;
+    uint32_t lo = 0xffffffffu, hi = 0u, lim = 0u;
     int need = kk, ab = 0;
+    bool hinted = false;
+    if (lim_hint != 0xffffffffu) {
+        const int bits = 32 - __clz(lim_hint);
+        const int sh = bits > 11 ? bits - 11 : 0;
+        for (int j = tid; j < kBins1; j += kThreads) sm.hist[j] = 0u;
+        __syncthreads();
+        int ca = 0, cb = 0;  // keys above / below the range
+        for (int i = tid; i < m4; i += kThreads) {
+            const uint4 v = k4[i];
+            const uint32_t k[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (4 * i + c < m) {
+                    if (k[c] < lo_hint) ++cb;
+                    else if (k[c] - lo_hint > lim_hint) ++ca;
+                    else atomicAdd(&sm.hist[(k[c] - lo_hint) >> sh], 1u);
+                }
+        }
+        ca = wave_sum_i(ca);
+        cb = wave_sum_i(cb);
+        if (lane == 0) {
+            sm.wgt[wv] = ca;
+            sm.weq[wv] = cb;
+        }
+        __syncthreads();
+        int ta = 0, tb = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            ta += sm.wgt[w];
+            tb += sm.weq[w];
+        }
+        if (tb == 0 && ta < kk && kk - ta <= m - ta) {
+            find_threshold(sm.hist, kBins1, kk - ta, sm);  // its barriers also retire wgt / weq
+            const uint32_t b = (uint32_t)sm.sel_bin;
+            const int a = sm.sel_above;
+            __syncthreads();
+            ab = ta + a;
+            need = kk - ta - a;
+            lo = lo_hint + (b << sh);
+            lim = min(lim_hint - (b << sh), (1u << sh) - 1u);
+            hinted = true;
+        } else {
+            __syncthreads();  // wgt / weq are reused below
+        }
+    }
+    if (!hinted) {
+        for (int i = tid; i < m4; i += kThreads) {
+            const uint4 v = k4[i];
+            const uint32_t k[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (4 * i + c < m) {
+                    lo = min(lo, k[c]);
+                    hi = max(hi, k[c]);
+                }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+            hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+        }
+        if (lane == 0) {
+            sm.wgt[wv] = (int)lo;
+            sm.weq[wv] = (int)hi;
+        }
+        __syncthreads();
+        lo = 0xffffffffu;
+        hi = 0u;
+        for (int w = 0; w < kWaves; ++w) {
+            lo = min(lo, (uint32_t)sm.wgt[w]);
+            hi = max(hi, (uint32_t)sm.weq[w]);
+        }
+        __syncthreads();
+        lim = hi - lo;
+    }
+    // the kk-th key lies in [lo, lo + lim]; `ab` keys lie above that range
     while (lim > 0) {
         const int bits = 32 - __clz(lim);
         const int sh = bits > 11 ? bits - 11 : 0;
@@ -674,14 +725,17 @@ union TopkSmem {
 };
 
 // The selection from a list of every candidate that can be selected (sm.key / sm.pos hold
-// nlist >= topk entries in any order; n is the row length, at most kFusedMaxLen): digits 2 and
-// 3 on the list give theta and the ties taken, then two position bitmaps give position order.
-__device__ void finish_from_list(FusedSmem& sm, int nlist, int topk, int n, int32_t* __restrict__ out) {
+// nlist >= topk entries in any order, every key at or above the first digit b1; n is the row
+// length, at most kFusedMaxLen): digits 2 and 3 on the list give theta and the ties taken,
+// then two position bitmaps give position order.
+__device__ void finish_from_list(FusedSmem& sm, int nlist, int topk, int n, int b1, int32_t* __restrict__ out) {
     const int tid = threadIdx.x;
-    // ---- digits 2 and 3 on the list: theta, and how many ties at theta are taken ----
+    // ---- digits 2 and 3 on the list: theta, and how many ties at theta are taken; theta has
+    // first digit b1 (keys 1 << 31 | (b1 - kHistBins) << 21 and the 2^21 - 1 after it) ----
     uint32_t theta;
     int above;
-    lds_kth_key(sm.key, nlist, topk, sm.sel, theta, above);
+    lds_kth_key(sm.key, nlist, topk, sm.sel, theta, above, 0x80000000u | ((uint32_t)(b1 - kHistBins) << 21),
+                (1u << 21) - 1u);
     const int need_eq = topk - above;
     // classes: 1 = above theta, 2 = tie at theta, 0 = not selected
     for (int j = tid; j < nlist; j += kThreads) {
@@ -748,24 +802,67 @@ __device__ void finish_from_list(FusedSmem& sm, int nlist, int topk, int n, int3
 
 // The first digit from a row's counts: the threshold digit b1 and the number of elements of
 // digit >= b1; false when the list path does not apply (fewer than topk counted scores, more
-// than kCap candidates, or a row longer than the bitmaps).  Ends with a barrier.
+// than kCap candidates, or a row longer than the bitmaps).  One wave does the search (lane l
+// holds bins 16l .. 16l+15, suffix sums over the lanes from the top), so the only barrier is
+// the one that hands the result to the other waves.  Ends with a barrier.
 __device__ bool threshold_from_counts(SelSmem& sel, const uint32_t* __restrict__ h, int n, int topk, int& b1,
                                       int& nlist) {
-    int cnt = 0;
-    for (int b = threadIdx.x; b < kHistBins; b += kThreads) {
-        const uint32_t c = h[b];
-        sel.hist[b] = c;
-        cnt += (int)c;
+    static_assert(kHistBins == 16 * kWave, "16 count bins per lane");
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        uint32_t c[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = *(const uint4*)(h + 16 * lane + 4 * q);
+            c[4 * q] = v.x;
+            c[4 * q + 1] = v.y;
+            c[4 * q + 2] = v.z;
+            c[4 * q + 3] = v.w;
+        }
+        int own = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) own += (int)c[j];
+        int suf = own;  // counts of this lane's bins and of every higher lane's
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int t = __shfl_down(suf, o);
+            if (lane + o < kWave) suf += t;
+        }
+        const int total = __shfl(suf, 0);
+        // the lane whose bins hold the topk-th largest counted score (none if total < topk)
+        if (lane == 0) {
+            sel.sel_bin = 0;
+            sel.sel_above = 0;
+            sel.wcnt[0] = 0;
+            sel.wcnt[1] = total;
+        }
+        int cum = suf - own;
+        if (cum < topk && topk <= suf) {
+            int bin = 16 * lane, above = cum, through = suf;
+            bool found = false;
+#pragma unroll
+            for (int j = 15; j >= 0; --j) {
+                if (!found && cum + (int)c[j] >= topk) {
+                    found = true;
+                    bin = 16 * lane + j;
+                    above = cum;
+                    through = cum + (int)c[j];
+                }
+                cum += (int)c[j];
+            }
+            sel.sel_bin = bin;
+            sel.sel_above = above;
+            sel.wcnt[0] = through;
+        }
     }
-    int total;
-    block_exclusive_scan(cnt, sel.wsum, total);  // also orders the histogram writes
+    __syncthreads();
+    const int total = sel.wcnt[1];
     bool fused = total >= topk && n <= kFusedMaxLen;
     b1 = 0;
     nlist = 0;
     if (fused) {
-        find_threshold(sel.hist, kHistBins, topk, sel);
         b1 = kHistBins + sel.sel_bin;
-        nlist = sel.sel_above + (int)sel.hist[sel.sel_bin];
+        nlist = sel.wcnt[0];
         fused = nlist <= kCap;
     }
     __syncthreads();  // every thread has read the threshold before the shared memory is reused
@@ -883,7 +980,7 @@ __global__ __launch_bounds__(kThreads, 2) void topk_hist_kernel(const float* __r
         append_step(e0, v);
     }
     __syncthreads();
-    finish_from_list(sm, nlist, topk, n, out);
+    finish_from_list(sm, nlist, topk, n, b1, out);
 }
 
 // Few long rows (decode): the list path split over segment workgroups.  Every workgroup of a
@@ -1023,7 +1120,7 @@ __global__ __launch_bounds__(kThreads, 2) void topk_list_finish_kernel(const flo
         }
     }
     __syncthreads();
-    finish_from_list(sm, nlist, topk, n, out);
+    finish_from_list(sm, nlist, topk, n, b1, out);
 }
 
 }  // namespace
