@@ -447,33 +447,47 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
         return hip_status(e);
     }
 
-    // Prefill: passes of `chunk` query rows per sequence.
+    // Prefill: passes of query rows per sequence.  A pass of R rows ending at row r1 takes
+    // [scores R x stride(r1) | idx R x topk | counts R x kHistBins] from the start of the
+    // workspace, stride(r1) the length of its last row (rounded up to 4), so early passes of a
+    // long sequence, whose rows are short, hold more rows than late ones; every pass takes as
+    // many rows as fit (a multiple of kRowGranule, or the rest of the sequence).  The rows'
+    // results do not depend on the passes.
     if (bt.pages != nullptr) return DSA_ERR_UNSUPPORTED;  // paged caches: decode batches only
-    const int64_t stride = score_stride_for(bt);
-    // the idx area is reserved even when idx_out is given (plan_forward's layout)
-    auto bytes_for = [&](int c) { return plan_forward(dims, shape, bt, c).total; };
-    // first estimate from the per-row areas; bytes_for then gives the exact size
-    const size_t per_row = (size_t)stride * sizeof(float) + (size_t)topk * 4 + kHistBins * 4;
-    int64_t c64 = (int64_t)(ws_bytes / per_row);
-    int chunk = (int)(c64 < bt.max_lq ? c64 : bt.max_lq);
-    if (chunk > kRowGranule) chunk -= chunk % kRowGranule;
-    while (chunk > 0 && bytes_for(chunk) > ws_bytes) chunk -= chunk > kRowGranule ? kRowGranule : 1;
-    const int min_chunk = bt.max_lq < kRowGranule ? bt.max_lq : kRowGranule;
-    if (chunk < 1 || chunk < min_chunk) return DSA_ERR_WORKSPACE;
-    const ForwardPlan p = plan_forward(dims, shape, bt, chunk);
-    float* sc = (float*)(wsb + p.scores_off);
-    int32_t* ix_ws = (int32_t*)(wsb + p.idx_off);
-    uint32_t* hs = (uint32_t*)(wsb + p.hist_off);
-    IndexerArgs ia{shape, q8, q_scale, w, k8, k_scale, sc, p.stride};
-    if (debug_log())
-        fprintf(stderr, "[dsa] prefill B=%d T=%d chunk=%d stride=%lld\n", bt.B, bt.T, chunk,
-                (long long)p.stride);
+    auto pass_bytes = [&](int64_t rows, int64_t stride_p) {
+        return align_up((size_t)(rows * stride_p) * sizeof(float)) + align_up((size_t)rows * topk * sizeof(int32_t)) +
+               align_up((size_t)rows * kHistBins * sizeof(uint32_t));
+    };
+    auto stride_to = [](int64_t len) { return (len + 3) & ~(int64_t)3; };
+    // the workspace must hold kRowGranule full-length rows (all rows of shorter sequences)
+    {
+        const int min_rows = bt.max_lq < kRowGranule ? bt.max_lq : kRowGranule;
+        if (pass_bytes(min_rows, score_stride_for(bt)) > ws_bytes) return DSA_ERR_WORKSPACE;
+    }
     for (int b = 0; b < bt.B; ++b) {
         const int lq = bt.lq(b), lk = bt.lk(b);
         const int qb = batch->cu_q_host[b], kb = batch->cu_k_host[b];
         const int pos0 = lk - lq;
-        for (int r0 = 0; r0 < lq; r0 += chunk) {
-            const int r1 = r0 + chunk < lq ? r0 + chunk : lq;
+        for (int r0 = 0; r0 < lq;) {
+            auto fits = [&](int rows) { return pass_bytes(rows, stride_to((int64_t)pos0 + r0 + rows)) <= ws_bytes; };
+            int rows = lq - r0;
+            if (!fits(rows)) {  // largest count that fits: fits() is monotone in the row count
+                int lo = 1, hi = rows - 1;
+                while (lo < hi) {
+                    const int mid = lo + (hi - lo + 1) / 2;
+                    if (fits(mid)) lo = mid; else hi = mid - 1;
+                }
+                rows = lo > kRowGranule ? lo - lo % kRowGranule : lo;
+                if (!fits(rows)) return DSA_ERR_WORKSPACE;
+            }
+            const int r1 = r0 + rows;
+            const int64_t stride = stride_to((int64_t)pos0 + r1);
+            float* sc = (float*)wsb;
+            int32_t* ix_ws = (int32_t*)(wsb + align_up((size_t)((int64_t)rows * stride) * sizeof(float)));
+            uint32_t* hs = (uint32_t*)((uint8_t*)ix_ws + align_up((size_t)rows * topk * sizeof(int32_t)));
+            if (debug_log())
+                fprintf(stderr, "[dsa] prefill seq %d rows %d..%d stride %lld\n", b, r0, r1, (long long)stride);
+            const IndexerArgs ia{shape, q8, q_scale, w, k8, k_scale, sc, stride};
             // rows with p + 1 <= topk keep every earlier position: no scores needed
             int rsel = topk - pos0;
             if (rsel < r0) rsel = r0;
@@ -483,18 +497,19 @@ dsa_status dsa_forward(const dsa_dims* dims, const dsa_batch* batch, const uint8
             if (rsel < r1) e = launch_zero_words(hrows, (int64_t)(r1 - rsel) * kHistBins, stream);
             if (e == hipSuccess && rsel < r1)
                 e = launch_indexer_prefill(ia, qb + rsel, r1 - rsel, pos0 + rsel, kb,
-                                           sc + (int64_t)(rsel - r0) * p.stride, stream, hrows);
+                                           sc + (int64_t)(rsel - r0) * stride, stream, hrows);
             int32_t* ix = idx_out ? idx_out + (int64_t)(qb + r0) * topk : ix_ws;
             RowMap map{nullptr, nullptr, 1, qb + r0, pos0 + r0, kb};
             // every row of the pass keeps all earlier positions (p + 1 <= k): dense causal
             // attention, and the index rows only if the caller asked for them
             const bool dense = pos0 + r1 <= topk;
             if (e == hipSuccess && (!dense || idx_out != nullptr))
-                e = launch_topk_from_hist(sc, p.stride, hs, ix, topk, map, r1 - r0, stream);
+                e = launch_topk_from_hist(sc, stride, hs, ix, topk, map, r1 - r0, stream);
             MqaArgs ma{shape, q, kv, ix, topk, out, lse, dims->sm_scale, dense ? IdxMode::Dense : IdxMode::Front};
             if (e == hipSuccess && !dense) e = debug_check(ix, topk, map, r1 - r0, stream);
             if (e == hipSuccess) e = launch_sparse_mqa(ma, map, r1 - r0, 1, nullptr, stream);
             if (e != hipSuccess) return DSA_ERR_HIP;
+            r0 = r1;
         }
     }
     return DSA_OK;
