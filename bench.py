@@ -197,10 +197,35 @@ def run_forward(c):
 
 
 def chunk_rows(c):
-    """Row passes of dsa_forward at the default workspace: 8192 rows each."""
-    L = c["L"]
-    ch = min(8192, L)
-    return [(r0, min(L, r0 + ch)) for r0 in range(0, L, ch)]
+    """Row passes of dsa_forward in the bench's workspace.  The library sizes each pass by area:
+    R rows ending at row r1 take R x round4(r1) fp32 scores plus R index rows and R count rows
+    (each area rounded up to 256 bytes) from the start of the workspace, and a pass takes as
+    many rows as fit (a multiple of 8, or the rest of the sequence)."""
+    L, k = c["L"], c["dims"].topk
+    ws = c["ws"].numel()
+
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def fits(r0, rows):
+        s = (r0 + rows + 3) // 4 * 4
+        return al(rows * s * 4) + al(rows * k * 4) + al(rows * dsa.COUNT_BINS * 4) <= ws
+
+    passes, r0 = [], 0
+    while r0 < L:
+        rows = L - r0
+        if not fits(r0, rows):
+            lo, hi = 1, rows - 1
+            while lo < hi:
+                mid = lo + (hi - lo + 1) // 2
+                if fits(r0, mid):
+                    lo = mid
+                else:
+                    hi = mid - 1
+            rows = lo - lo % 8 if lo > 8 else lo
+        passes.append((r0, r0 + rows))
+        r0 += rows
+    return passes
 
 
 def stage_breakdown(c, reps=1):
@@ -212,11 +237,9 @@ def stage_breakdown(c, reps=1):
     k = dims.topk
     dev = inp["q8"].device
     passes = chunk_rows(c)
-    ch = passes[0][1] - passes[0][0]
-    stride = (L + 3) // 4 * 4
-    scores = c["ws"][: ch * stride * 4].view(torch.float32).view(ch, stride)
-    idx = torch.empty(ch, k, dtype=torch.int32, device=dev)
-    counts = torch.empty(ch, dsa.COUNT_BINS, dtype=torch.int32, device=dev)
+    ch = max(r1 - r0 for r0, r1 in passes)
+    idx_all = torch.empty(ch, k, dtype=torch.int32, device=dev)
+    counts_all = torch.empty(ch, dsa.COUNT_BINS, dtype=torch.int32, device=dev)
     kl = torch.empty(L, dtype=torch.float32, device=dev)
     t_kl, n_kl = 0.0, 0
     t = {"indexer": 0.0, "topk": 0.0, "mqa": 0.0}
@@ -228,6 +251,10 @@ def stage_breakdown(c, reps=1):
         t0 = dict(t)
         for r0, r1 in passes:
             n = r1 - r0
+            # the pass's score rows at its own stride (its last row's length), as in dsa_forward
+            stride = (r1 + 3) // 4 * 4
+            scores = c["ws"][: n * stride * 4].view(torch.float32).view(n, stride)
+            idx, counts = idx_all[:n], counts_all[:n]
             # the pass as its own batch: queries r0..r1-1 are the last n of keys 0..r1-1
             b = dsa.Batch([0, n], [0, r1], device=dev)
             rsel = max(r0, k)  # rows with p + 1 <= k need no scores
