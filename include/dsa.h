@@ -89,8 +89,12 @@ typedef struct {
 } dsa_batch;
 
 /* Bytes of workspace that dsa_forward uses by default for this batch (also enough for
- * dsa_sparse_mqa and dsa_dense_mqa on the whole batch).  dsa_forward also accepts a smaller workspace down to
- * dsa_workspace_min; it then processes fewer query rows per pass. */
+ * dsa_sparse_mqa and dsa_dense_mqa on the whole batch): room for the scores, index rows and
+ * score counts of 8192 query rows of the longest sequence.  dsa_forward runs a prefill in
+ * passes of query rows sized by area, each as many rows as the workspace holds at the pass's
+ * own row length, so early passes of a long sequence take more (shorter) rows.  It also
+ * accepts a smaller workspace down to dsa_workspace_min (8 rows of the longest sequence);
+ * the passes then hold fewer rows.  Results do not depend on the workspace size. */
 dsa_status dsa_workspace_size(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
 dsa_status dsa_workspace_min(const dsa_dims* dims, const dsa_batch* batch, size_t* bytes);
 
