@@ -257,6 +257,7 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     __shared__ uint32_t rofs[C::RING][kBlk];   // row byte offsets of staged blocks
     __shared__ uint32_t rmask[C::RING];        // per staged block: bit j = slot j holds a row
     __shared__ float fin_l[2][32];             // softmax denominators at the end
+    __shared__ int32_t rid[C::RING][kWave];    // index slots of blocks fetched ahead for staging
 
     // Work item.  With two workgroups per row (64 heads each) the pair is issued 8 ids
     // apart, i.e. onto the same XCD, so the second gather of each latent row hits its L2.
@@ -293,7 +294,8 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
 
     // Row offsets (packed: byte offset from the sequence's first row; paged: pool row) and
     // occupancy of block b, staged in ring slot b % RING: the first RING blocks here, the rest
-    // by wave 0 one step before the loads need them.  Slots that slot_row rejects (-1, values
+    // by value wave 2 at the end of the step before the loads need them.  Slots that slot_row
+    // rejects (-1, values
     // outside the sequence, page ids outside a pool of known size) are empty: row 0 is loaded
     // in their place and zeroed, so no load ever leaves the caches.
     auto stage = [&](int b, int id) {  // lanes 0..31 hold the ids of the block's slots
@@ -508,20 +510,12 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
             for (int u = 0; u < 2; ++u) lds_write16(p_own + u * (kWave * 16), __builtin_bit_cast(v4i, pf[u]));
         };
         if (nblk > 0) {
-            // wave 0 stages the row offsets of block b + RING during step b, from ids it loaded
-            // one step earlier (it issues no other global loads)
-            const bool stager = wv == 0;
-            int ids = stager && C::RING < nblk ? load_ids(C::RING) : -1;
             lds_barrier();  // block 0 visible
             v16f s0 = half_logits(0, std::true_type{});
             lds_barrier();  // mid-step of the prologue: block 0's second half visible
             softmax(0, s0);
             lds_barrier();  // end of the prologue: block 0's P^T visible
             for (int blk = 0; blk < nblk; ++blk) {
-                if (stager && blk + C::RING < nblk) {
-                    stage(blk + C::RING, ids);
-                    ids = blk + C::RING + 1 < nblk ? load_ids(blk + C::RING + 1) : -1;
-                }
                 const bool next = blk + 1 < nblk;
                 if (next) s0 = half_logits(blk + 1, std::true_type{});
                 lds_barrier();  // mid-step: block blk+1's second half visible
@@ -624,12 +618,43 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
         lds_barrier();  // block 0 visible
         lds_barrier();  // mid-step of the prologue
         lds_barrier();  // end of the prologue: block 0's P^T visible
+        // Value wave 2 stages the row offsets of block b + RING at the end of step b (after its
+        // MFMAs; the value waves wait at the end barrier anyway; on a logit wave the staging sat
+        // on the step's critical path).  It fetches each block's index slots IDS_AHEAD steps
+        // before staging it, with direct loads into rid, so the wait for them rarely waits;
+        // it issues no other global loads, so its load counter holds only these fetches.
+        const bool stager = vq == 0;
+        constexpr int IDS_AHEAD = 3;
+        static_assert(IDS_AHEAD < C::RING, "the fetch slot of block b + IDS_AHEAD is free");
+        auto fetch_ids = [&](int b) {  // lanes < kBlk: block b's slots -> rid[b % RING]
+            const int j = j0 + b * kBlk + lane;
+            if (lane < kBlk && j < j1) dma4(irow, (uint32_t)j * 4u, lds_addr(&rid[b % C::RING][0]));
+        };
+        if (stager && !dense)
+            for (int b = C::RING; b < nblk && b < C::RING + IDS_AHEAD; ++b) fetch_ids(b);
         for (int blk = 0; blk < nblk; ++blk) {
             v8bf pf[2][2];
             take_p(pf);
             values(blk, 0, pf);
             lds_barrier();  // mid-step
             values(blk, 1, pf);
+            if (stager && blk + C::RING < nblk) {
+                const int b = blk + C::RING;
+                const int j = j0 + b * kBlk + lane;
+                int id = -1;
+                if (dense) {
+                    if (lane < kBlk && j < j1) id = j;
+                } else {
+                    // block b's fetch has landed once only the younger fetches may still fly
+                    const int younger = min(nblk - 1, b + IDS_AHEAD - 1) - b;
+                    if (younger >= 2) wait_loads<2>();
+                    else if (younger == 1) wait_loads<1>();
+                    else wait_loads<0>();
+                    if (lane < kBlk && j < j1) id = rid[b % C::RING][lane];
+                }
+                stage(b, id);
+                if (!dense && b + IDS_AHEAD < nblk) fetch_ids(b + IDS_AHEAD);
+            }
             lds_barrier();  // end of step blk
         }
     }
