@@ -375,13 +375,16 @@ def test_forward_prod_16k_sampled(cuda):
 
 
 def test_forward_small_workspace_is_identical(cuda):
-    say("forward prod L=3000 default vs minimal workspace (bit-identical)")
+    say("forward prod L=3000 default vs minimal and a third of the default workspace (bit-identical)")
     dims = dsa_inputs.PROD
     inp = dsa_inputs.prefill_inputs(3000, dims, seed=2, device=cuda)
     o1, l1, i1 = run_forward(inp, dims, cuda)
     batch = dsa.Batch(inp["cu_q"], inp["cu_k"], device=cuda)
     o2, l2, i2 = run_forward(inp, dims, cuda, ws_bytes=dsa.workspace_min(dims, batch))
     assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+    # a third of the default: three passes of different row counts at different score strides
+    o4, l4, i4 = run_forward(inp, dims, cuda, ws_bytes=dsa.workspace_size(dims, batch) // 3)
+    assert torch.equal(i1, i4) and torch.equal(o1, o4) and torch.equal(l1, l4)
     o3, l3, i3 = run_forward(inp, dims, cuda)  # determinism
     assert torch.equal(i1, i3) and torch.equal(o1, o3) and torch.equal(l1, l3)
 
