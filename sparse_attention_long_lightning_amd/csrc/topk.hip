@@ -1001,9 +1001,6 @@ __global__ __launch_bounds__(kThreads, 2) void topk_list_append_kernel(const flo
     const int n = row_info(map, row).pos + 1;
     const int s0 = blockIdx.x * kSeg;
     if (n <= topk || s0 >= n) return;
-    int b1, nlist;
-    if (!threshold_from_counts(sel, hist + (int64_t)row * kHistBins, n, topk, b1, nlist)) return;
-    const float thr = list_threshold(b1);
     const float* x = scores + (int64_t)row * stride;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     constexpr int kPerWave = kSeg / kWaves;  // whole steps of 256 * kUnroll elements
@@ -1012,7 +1009,8 @@ __global__ __launch_bounds__(kThreads, 2) void topk_list_append_kernel(const flo
     const int sb = min(n, s0 + wv * kPerWave), se = min(n, sb + kPerWave);
     // the wave's scores stay in registers: they are counted first, so that the workgroup
     // reserves its list space with one atomic (atomics of many waves on one row's counter
-    // serialize), then placed
+    // serialize), then placed.  They are loaded before the threshold is known, so the row's
+    // count read and the score reads are in flight together.
     float v[kSteps][kUnroll][4];
 #pragma unroll
     for (int st = 0; st < kSteps; ++st)
@@ -1030,6 +1028,9 @@ __global__ __launch_bounds__(kThreads, 2) void topk_list_append_kernel(const flo
                 for (int c = 0; c < 4; ++c) v[st][u][c] = e + c < se ? x[e + c] : -INFINITY;
             }
         }
+    int b1, nlist;
+    if (!threshold_from_counts(sel, hist + (int64_t)row * kHistBins, n, topk, b1, nlist)) return;
+    const float thr = list_threshold(b1);
     int cnt = 0;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st)
