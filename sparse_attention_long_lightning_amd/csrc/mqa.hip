@@ -73,9 +73,10 @@ struct MqaCfg {
     //   waves 0, 1        logits over the first half of the dims for head group 0 / 1
     //                     (32 heads each), then the online softmax of the group
     //   waves 4, 5        logits over the second half of the dims of the same group,
-    //                     handed to wave w - 4 through LDS, and the direct global->LDS loads
-    //                     of the gathered rows
-    //   waves 2, 3, 6, 7  value product (64 heads x a quarter of the DV dims each)
+    //                     handed to wave w - 4 through LDS, and most of the direct
+    //                     global->LDS loads of the gathered rows
+    //   waves 2, 3, 6, 7  value product (64 heads x a quarter of the DV dims each); waves
+    //                     3, 6, 7 also issue the rest of the direct loads
     // Splitting each group's logits over two waves of one SIMD halves the LDS operand bytes
     // each wave must read per block (a single wave's LDS read rate is the limit otherwise).
     static constexpr int THREADS = 512;
@@ -95,8 +96,15 @@ struct MqaCfg {
     static constexpr int INSTRS = RV::INSTRS + RR::INSTRS;
     static constexpr int ROW_BYTES = DQK * 2;              // bytes of one latent row in memory
     static constexpr int VBYTES = DV * 2;                  // bytes of its value part
-    static constexpr int MAXK = (INSTRS + NDW - 1) / NDW;  // direct loads per loading wave and block
-    static constexpr int LOADS_PER_WAVE = INSTRS / NDW;    // fewest of a loading wave per block
+    // Direct-load instructions of a block: waves 4, 5 issue the first HLOAD of them, value
+    // waves 3, 6, 7 the last VLOAD (blocks of the production shape only: small test shapes
+    // leave every load to waves 4, 5)
+    static constexpr int NVL = 3;                                    // value waves that load
+    static constexpr int VLOAD = (INSTRS >= 24 && NVW == 4) ? 6 : 0;
+    static constexpr int HLOAD = INSTRS - VLOAD;
+    static constexpr int MAXK = (HLOAD + NDW - 1) / NDW;  // direct loads per helper wave and block
+    static constexpr int LOADS_PER_WAVE = HLOAD / NDW;    // fewest of a helper wave per block
+    static constexpr int VMAXK = VLOAD > 0 ? VLOAD / NVL : 1;  // per loading value wave and block
     static constexpr int QK_AHEAD = KH < 9 ? KH : 9;       // logit operand reads kept in flight
     // Per-lane LDS offsets are kept for TLQ logit slices and TLV value tiles only: the rest
     // differ by a multiple of the swizzle period and reach the reads as immediate offsets.
@@ -106,6 +114,7 @@ struct MqaCfg {
     static_assert(DQK % 16 == 0 && DV % 64 == 0 && VT % NVW == 0, "unsupported latent widths");
     static_assert(NHH <= 2, "at most 128 heads");
     static_assert(3 * MAXK <= 63, "direct loads of three blocks must fit the load counter");
+    static_assert(VLOAD % NVL == 0, "loading value waves issue equal shares");
 };
 
 __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
@@ -176,35 +185,35 @@ __device__ __forceinline__ void piece_of(int I, int lane, int& r, int& col, int&
 }
 
 
-// Issues the direct global->LDS loads of one block of kBlk latent rows into the buffer at
-// LDS address `buf`; `offs` points at the block's kBlk staged rows in LDS (empty slots hold
-// row 0, and are zeroed by zero_empty_rows once landed).  Packed caches stage byte offsets from
-// the sequence's first row (32 bits: a sequence is shorter than 2^32 / 1152 positions, checked
-// on the host) and load from the scalar base kvb; paged caches stage pool rows and load from
-// 64-bit per-lane addresses, so a page pool may exceed 4 GiB.  Load wave dw owns instructions
-// I = dw + NDW*k, fixed at compile time, so the sequence is fully unrolled: all offset reads
-// first, then the loads.
-template <class C, bool PAGED>
-__device__ __forceinline__ void issue_block(uint32_t buf, const uint8_t* kvb, const uint32_t* offs,
-                                            int dw, int lane) {
-    constexpr bool FULL = C::INSTRS % C::NDW == 0;  // every load wave has MAXK slots
+// Issues direct global->LDS loads of one block of kBlk latent rows into the buffer at LDS
+// address `buf`; `offs` points at the block's kBlk staged rows in LDS (empty slots hold row
+// 0, and are zeroed by zero_pieces once landed).  Packed caches stage byte offsets from the
+// sequence's first row (32 bits: a sequence is shorter than 2^32 / 1152 positions, checked on
+// the host) and load from the scalar base kvb; paged caches stage pool rows and load from
+// 64-bit per-lane addresses, so a page pool may exceed 4 GiB.  The calling wave owns
+// instructions I = first + STEP*k (k < N) below lim, a pattern fixed at compile time per wave
+// kind, so the sequence is fully unrolled: all offset reads first, then the loads.  FULL:
+// every one of the N instructions is below lim.
+template <class C, bool PAGED, int N, int STEP, bool FULL>
+__device__ __forceinline__ void issue_pieces(uint32_t buf, const uint8_t* kvb, const uint32_t* offs,
+                                             int first, int lim, int lane) {
     using Off = typename std::conditional<PAGED, const uint8_t*, uint32_t>::type;
-    Off o[C::MAXK];
+    Off o[N];
 #pragma unroll
-    for (int k = 0; k < C::MAXK; ++k) {
-        const int I = dw + C::NDW * k;
+    for (int k = 0; k < N; ++k) {
+        const int I = first + STEP * k;
         int r, col, base;
         piece_of<C>(I, lane, r, col, base);
-        const bool live = FULL || I < C::INSTRS;
+        const bool live = FULL || I < lim;
         if constexpr (PAGED)
             o[k] = kvb + (live ? (uint64_t)offs[r] * C::ROW_BYTES + col : 0);
         else
             o[k] = live ? offs[r] + col : 0u;
     }
 #pragma unroll
-    for (int k = 0; k < C::MAXK; ++k) {
-        const int I = dw + C::NDW * k;
-        if (FULL || I < C::INSTRS) {
+    for (int k = 0; k < N; ++k) {
+        const int I = first + STEP * k;
+        if (FULL || I < lim) {
             int r, col, base;
             piece_of<C>(I, lane, r, col, base);
             if constexpr (PAGED)
@@ -215,15 +224,15 @@ __device__ __forceinline__ void issue_block(uint32_t buf, const uint8_t* kvb, co
     }
 }
 
-// Zeroes the pieces of empty rows that this load wave moved itself (so the direct load has
-// landed before the store, in this wave's program order).  Empty rows then contribute exact
-// zeros to both products whatever row 0 of the sequence holds.
-template <class C>
-__device__ __forceinline__ void zero_empty_rows(uint32_t buf, uint32_t vmask, int dw, int lane) {
+// Zeroes the pieces of empty rows that this wave loaded itself with issue_pieces (so the
+// direct load has landed before the store, in this wave's program order).  Empty rows then
+// contribute exact zeros to both products whatever row 0 of the sequence holds.
+template <class C, int N, int STEP>
+__device__ __forceinline__ void zero_pieces(uint32_t buf, uint32_t vmask, int first, int lim, int lane) {
 #pragma unroll
-    for (int k = 0; k < C::MAXK; ++k) {
-        const int I = dw + C::NDW * k;
-        if (I < C::INSTRS) {
+    for (int k = 0; k < N; ++k) {
+        const int I = first + STEP * k;
+        if (I < lim) {
             int r, col, base;
             piece_of<C>(I, lane, r, col, base);
             if (!((vmask >> r) & 1u)) lds_write16(buf + base + 16 * lane, (v4i){0, 0, 0, 0});
@@ -231,12 +240,12 @@ __device__ __forceinline__ void zero_empty_rows(uint32_t buf, uint32_t vmask, in
     }
 }
 
-// Waits until at most N direct loads of this wave are outstanding, N chosen at run time
-// among the counts the pipeline uses.
-template <class C>
+// Waits until at most nb blocks' worth of direct loads (PER per block) of this wave are
+// outstanding, nb chosen at run time among the counts the pipeline uses.
+template <int PER>
 __device__ __forceinline__ void wait_blocks_left(int nb) {
-    if (nb >= 2) wait_loads<2 * C::LOADS_PER_WAVE>();
-    else if (nb == 1) wait_loads<C::LOADS_PER_WAVE>();
+    if (nb >= 2) wait_loads<2 * PER>();
+    else if (nb == 1) wait_loads<PER>();
     else wait_loads<0>();
 }
 
@@ -333,12 +342,14 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
     //                 second half, run the online softmax and publish block b+1's P^T and
     //                 rescale factors
     //   waves 4, 5:   hand over the second half of block b+1 (computed in step b-1); issue
-    //                 the direct loads of block b+3 into the buffer block b-1 used and wait
-    //                 for block b+2; after the mid-step barrier, the second half of block
-    //                 b+2, so that these MFMAs run beside the softmax of waves 0, 1 on the
-    //                 same SIMD
+    //                 their direct loads of block b+3 into the buffer block b-1 used and wait
+    //                 for their loads of block b+2; after the mid-step barrier, the second
+    //                 half of block b+2, so that these MFMAs run beside the softmax of waves
+    //                 0, 1 on the same SIMD
     //   value waves:  read block b's P^T (published in step b-1); rescale O if needed and
-    //                 O^T += V^T P^T for block b, half on each side of the mid-step barrier
+    //                 O^T += V^T P^T for block b, half on each side of the mid-step barrier;
+    //                 waves 3, 6, 7 wait for their loads of block b+2 before the mid-step
+    //                 barrier and issue those of block b+3 after their second half
     //   end barrier:  block b+1's P^T is visible; block b's buffer is free
     if (wv != 2 && wv != 3 && wv != 6 && wv != 7) {
         // ---------------- logits (and softmax on waves 0, 1) ----------------
@@ -412,22 +423,25 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
                                 __builtin_bit_cast(v4i, (v4f){sp[4 * r4], sp[4 * r4 + 1], sp[4 * r4 + 2],
                                                               sp[4 * r4 + 3]}));
             };
-            const int dw = hg;  // direct-load slot
+            // direct loads I = hg + 2k below HLOAD of each block
             auto land = [&](int blk) {  // block blk's loads have landed for this wave: zero its empty rows
                 const uint32_t vm = rmask[blk % C::RING];
-                if (vm != 0xffffffffu) zero_empty_rows<C>(buf_of(blk), vm, dw, lane);
+                if (vm != 0xffffffffu) zero_pieces<C, C::MAXK, C::NDW>(buf_of(blk), vm, hg, C::HLOAD, lane);
             };
-            auto issue = [&](int blk) { issue_block<C, PAGED>(buf_of(blk), kvb, rofs[blk % C::RING], dw, lane); };
+            auto issue = [&](int blk) {
+                issue_pieces<C, PAGED, C::MAXK, C::NDW, C::HLOAD % C::NDW == 0>(buf_of(blk), kvb,
+                                                                                rofs[blk % C::RING], hg, C::HLOAD, lane);
+            };
             if (nblk > 0) {
                 issue(0);
                 if (nblk > 1) issue(1);
                 if (nblk > 2) issue(2);
-                wait_blocks_left<C>(min(nblk, 3) - 1);
+                wait_blocks_left<C::LOADS_PER_WAVE>(min(nblk, 3) - 1);
                 land(0);
                 lds_barrier();  // block 0 visible
                 publish(half_logits(0, std::false_type{}));
                 if (nblk > 1) {
-                    wait_blocks_left<C>(min(nblk, 3) - 2);
+                    wait_blocks_left<C::LOADS_PER_WAVE>(min(nblk, 3) - 2);
                     land(1);
                 }
                 lds_barrier();  // mid-step of the prologue: block 1's rows visible
@@ -438,7 +452,7 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
                     const bool more = blk + 3 < nblk;
                     if (more) issue(blk + 3);  // into the buffer block blk-1 used
                     if (blk + 2 < nblk) {
-                        wait_blocks_left<C>(more ? 1 : 0);
+                        wait_blocks_left<C::LOADS_PER_WAVE>(more ? 1 : 0);
                         land(blk + 2);
                     }
                     lds_barrier();  // mid-step: block blk+2's rows visible
@@ -614,9 +628,36 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
         lds_barrier();
         return;
     }
+    // Value waves 3, 6, 7 (quarters 1..3) issue the last VLOAD direct loads of each block,
+    // I = HLOAD + vq - 1 + 3k: those of block b+3 after the second value half of step b (the
+    // buffer block b-1 used; a value wave would otherwise wait at the end barrier there), and
+    // they wait for block b+2's before the mid-step barrier of step b, where waves 4, 5 wait
+    // for theirs.  Fewer loads then sit in the helpers' phase before that barrier.  These are
+    // the only global loads of these waves, so their load counter holds only these.
+    const bool loader = C::VLOAD > 0 && vq > 0;
+    const int vfirst = C::HLOAD + vq - 1;
+    auto vland = [&](int blk) {
+        const uint32_t vm = rmask[blk % C::RING];
+        if (vm != 0xffffffffu) zero_pieces<C, C::VMAXK, C::NVL>(buf_of(blk), vm, vfirst, C::INSTRS, lane);
+    };
+    auto vissue = [&](int blk) {
+        issue_pieces<C, PAGED, C::VMAXK, C::NVL, (C::VLOAD > 0)>(buf_of(blk), kvb, rofs[blk % C::RING], vfirst, C::INSTRS, lane);
+    };
+    constexpr int VPER = C::VMAXK;
     if (nblk > 0) {
+        if (loader) {
+            vissue(0);
+            if (nblk > 1) vissue(1);
+            if (nblk > 2) vissue(2);
+            wait_blocks_left<VPER>(min(nblk, 3) - 1);
+            vland(0);
+        }
         lds_barrier();  // block 0 visible
-        lds_barrier();  // mid-step of the prologue
+        if (loader && nblk > 1) {
+            wait_blocks_left<VPER>(min(nblk, 3) - 2);
+            vland(1);
+        }
+        lds_barrier();  // mid-step of the prologue: block 1 visible
         lds_barrier();  // end of the prologue: block 0's P^T visible
         // Value wave 2 stages the row offsets of block b + RING at the end of step b (after its
         // MFMAs; the value waves wait at the end barrier anyway; on a logit wave the staging sat
@@ -636,8 +677,13 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
             v8bf pf[2][2];
             take_p(pf);
             values(blk, 0, pf);
-            lds_barrier();  // mid-step
+            if (loader && blk + 2 < nblk) {  // only block blk+2's loads are in flight
+                wait_loads<0>();
+                vland(blk + 2);
+            }
+            lds_barrier();  // mid-step: block blk+2 visible
             values(blk, 1, pf);
+            if (loader && blk + 3 < nblk) vissue(blk + 3);
             if (stager && blk + C::RING < nblk) {
                 const int b = blk + C::RING;
                 const int j = j0 + b * kBlk + lane;
