@@ -742,40 +742,68 @@ __global__ __launch_bounds__(512, 1) void sparse_mqa_kernel(
 }
 
 // Merges the split partials of each (row, head): weights 2^(m_j - M) on the unnormalised
-// partial outputs and sums.
+// partial outputs and sums, splits in ascending order.  Every split's (m, l) and partial
+// output of the head are loaded before any is used, so the merge waits for one round of
+// loads rather than one per split.  Lane l holds dims 4l..4l+3 of each 256-dim slice.
+constexpr int kMaxSplit = 8;
 template <int H, int DV>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(const float* __restrict__ part_o,
                                                           const float2* __restrict__ part_ml,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse, RowMap map,
                                                           int n_rows, int n_split) {
+    static_assert(DV % 256 == 0 || DV == 64, "value width");
+    constexpr int NV = DV >= 256 ? DV / 256 : 1;  // 4-float pieces per lane and split
     const int row = blockIdx.x;
     const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (row >= n_rows || head >= H) return;
     const int lane = threadIdx.x & 63;
+    const bool live = DV >= 256 || lane < DV / 4;
     const RowInfo ri = row_info(map, row);
-    float M = -INFINITY;
-    for (int j = 0; j < n_split; ++j) M = fmaxf(M, part_ml[((int64_t)row * n_split + j) * H + head].x);
-    float L = 0.f;
-    float acc[DV / 64];
+    float2 ml[kMaxSplit];
+    v4f po[kMaxSplit][NV];
 #pragma unroll
-    for (int i = 0; i < DV / 64; ++i) acc[i] = 0.f;
-    if (M != -INFINITY) {
-        for (int j = 0; j < n_split; ++j) {
+    for (int j = 0; j < kMaxSplit; ++j) {
+        ml[j] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) po[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};
+        if (j < n_split) {
             const int64_t item = (int64_t)row * n_split + j;
-            const float2 ml = part_ml[item * H + head];
-            if (ml.x == -INFINITY) continue;
-            const float wgt = exp2f(ml.x - M);
-            L += ml.y * wgt;
+            ml[j] = part_ml[item * H + head];
             const float* op = part_o + (item * H + head) * DV;
 #pragma unroll
-            for (int i = 0; i < DV / 64; ++i) acc[i] += wgt * op[lane + 64 * i];
+            for (int i = 0; i < NV; ++i)
+                if (live) po[j][i] = *(const v4f*)(op + 256 * i + 4 * lane);
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMaxSplit; ++j) M = fmaxf(M, ml[j].x);
+    float L = 0.f;
+    v4f acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < kMaxSplit; ++j) {
+            if (ml[j].x == -INFINITY) continue;  // also the splits past n_split
+            const float wgt = exp2f(ml[j].x - M);
+            L += ml[j].y * wgt;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[i][c] += wgt * po[j][i][c];
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint16_t* o = out + ((int64_t)ri.qrow * H + head) * DV;
 #pragma unroll
-    for (int i = 0; i < DV / 64; ++i) o[lane + 64 * i] = f2bf(acc[i] * inv);
+    for (int i = 0; i < NV; ++i)
+        if (live) {
+            const uint32_t w0 = (uint32_t)f2bf(acc[i][0] * inv) | ((uint32_t)f2bf(acc[i][1] * inv) << 16);
+            const uint32_t w1 = (uint32_t)f2bf(acc[i][2] * inv) | ((uint32_t)f2bf(acc[i][3] * inv) << 16);
+            *(v2i*)(o + 256 * i + 4 * lane) = (v2i){(int)w0, (int)w1};
+        }
     if (lse != nullptr && lane == 0)
         lse[(int64_t)ri.qrow * H + head] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
@@ -799,6 +827,7 @@ hipError_t launch_t(const MqaArgs& a, const RowMap& map, int n_rows, int n_split
                            a.lse, nullptr, nullptr, map, n_rows, 1, sm_log2, (int)a.mode);
         return hipGetLastError();
     }
+    if (n_split > kMaxSplit) return hipErrorInvalidValue;  // the combine holds kMaxSplit splits
     float* part_o = (float*)ws;
     float2* part_ml = (float2*)(part_o + (size_t)n_rows * n_split * H * DV);
     auto kern = paged ? sparse_mqa_kernel<H, DQK, DV, true, true> : sparse_mqa_kernel<H, DQK, DV, true, false>;
