@@ -79,8 +79,9 @@ constexpr int kIxThreads = 768;  // 12 waves: three per SIMD, so one wave's epil
                                  // the other's MFMAs
 constexpr int kIxWaves = kIxThreads / kWave;
 constexpr int kIxTile = 256;     // keys per LDS tile
-constexpr int kIxSeg = 4096;     // keys per workgroup: a run of tiles through a 3-deep ring
+constexpr int kIxSeg = 8192;     // keys per workgroup: a run of tiles through a 3-deep ring
 constexpr int kIxBufs = 3;
+static_assert(kIxSeg % kIxTile == 0 && kIxSeg < 65536, "whole tiles; a segment's counts fit 16-bit bins");
 
 // LDS image of one key tile: kIxTile rows of D FP8 bytes, 16-byte chunks XOR-swizzled per row
 // (the direct loads write 1 KiB contiguous pieces, so the swizzle is applied to which global

@@ -80,7 +80,7 @@ struct MqaCfg {
     // Splitting each group's logits over two waves of one SIMD halves the LDS operand bytes
     // each wave must read per block (a single wave's LDS read rate is the limit otherwise).
     static constexpr int THREADS = 512;
-    static constexpr int NDW = 2;              // waves issuing direct loads
+    static constexpr int NDW = 2;              // helper waves issuing direct loads
     static constexpr int NBUF = 4;             // gathered blocks resident in LDS
     static constexpr int RING = 4;             // blocks of row offsets staged in LDS
     static constexpr int NHH = (H + 63) / 64;  // workgroups per query row, 64 heads each
